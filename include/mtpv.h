@@ -1,0 +1,219 @@
+/*
+ * mtpv.h - C ABI of the vocab-side draft-and-verify step of MTP speculative
+ * decoding, built for AMD MI355X (gfx950) with hand-written HIP kernels.
+ *
+ * What the calls compute. The target model has produced hidden states for the
+ * k+1 verify positions of each of B requests, and the MTP drafter has proposed k
+ * draft tokens per request. One vocabulary head W_lm [V, H], shared by the main
+ * model and the MTP drafter ("The Tiny Draft Model Hidden Inside Qwen", sections
+ * "One step deeper than the main model" and "What vLLM and SGLang do with the
+ * weights"; "Optimize vLLM speculative decoding with FastMTP heads", section "Key
+ * features"), is streamed from HBM once per call to produce the logits of every
+ * row; the calls then take a distribution at every position, keep the longest
+ * prefix of drafts the target agrees with, and replace the first rejected slot
+ * with a draw from the corrected distribution ("The Tiny Draft Model Hidden Inside
+ * Qwen", section "How the draft becomes real output"; "Speculative Decoding and
+ * MTP: Why Guessing Is Free", sections "Speculative decoding: draft, then verify"
+ * and "It's exact, not approximate").
+ *
+ * Notation. B requests, k drafts per request, H hidden width, V vocabulary size,
+ * T temperature. Slot j of request b: p_j = softmax(l(target row j) / T) for
+ * j = 0..k, q_j = softmax(l(drafter row j) / T) for j = 0..k-1. Draft
+ * draft_tokens[b*k + j] is judged against p_j; p_k only feeds the bonus token.
+ *
+ * Conventions for every call:
+ *  - All array arguments are DEVICE pointers owned by the caller, row-major and
+ *    contiguous, 16-byte aligned. The library allocates nothing per call.
+ *  - dtype selects the storage of hidden states and W_lm: MTPV_BF16 (bf16) or
+ *    MTPV_F32 (fp32). Accumulation is fp32 in both cases; sampling math is fp64.
+ *  - H must be a multiple of 8 (whole 16-byte loads per row); V >= 1; B >= 1;
+ *    0 <= k <= 64.
+ *  - stream is a hipStream_t passed as void* (NULL = the default stream). Calls
+ *    are asynchronous and stream ordered; nothing synchronizes the host.
+ *  - workspace is caller-owned device memory of at least
+ *    mtpv_workspace_bytes(mode, B, k, H, V, dtype) bytes, 256-byte aligned. Its
+ *    contents need no initialisation and are scratch between calls; two calls
+ *    in flight at once must not share one workspace.
+ *  - Errors in sizes, pointers, alignment, dtype or workspace are found on the
+ *    host before anything is enqueued and returned as a negative mtpv_status.
+ *    A draft id outside [0, V) is not a host error (drafts live on the device):
+ *    that draft counts as rejected and the call's device error word gets
+ *    MTPV_DEVERR_DRAFT_RANGE (read it with mtpv_device_error).
+ *  - No exception crosses this boundary.
+ */
+#ifndef MTPV_H_
+#define MTPV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define MTPV_API __attribute__((visibility("default")))
+#else
+#define MTPV_API
+#endif
+
+typedef enum mtpv_status {
+    MTPV_OK = 0,
+    MTPV_EINVAL = -1,     /* a size or scalar is out of range (B < 1, k < 0, T <= 0, ...) */
+    MTPV_EALIGN = -2,     /* H not a multiple of 8, or a pointer not 16-byte aligned   */
+    MTPV_EWORKSPACE = -3, /* workspace NULL, misaligned or smaller than required       */
+    MTPV_EDTYPE = -4,     /* dtype is neither MTPV_BF16 nor MTPV_F32                   */
+    MTPV_ENULL = -5,      /* a required pointer is NULL                                */
+    MTPV_ELAUNCH = -6,    /* a kernel launch failed                                    */
+    MTPV_EDEVICE = -7     /* HIP runtime error (no device, bad stream, copy failed)    */
+} mtpv_status;
+
+typedef enum mtpv_dtype { MTPV_BF16 = 0, MTPV_F32 = 1 } mtpv_dtype;
+
+/* Which call a workspace is sized for. */
+typedef enum mtpv_mode { MTPV_MODE_GREEDY = 0, MTPV_MODE_SAMPLE = 1, MTPV_MODE_DRAFT = 2 } mtpv_mode;
+
+/* Bits of the per-call device error word. */
+#define MTPV_DEVERR_DRAFT_RANGE 1 /* some draft id was outside [0, V); it was rejected */
+
+/*
+ * Optional exports for parity tests; pass NULL (or NULL members) in production.
+ * Rows are numbered as the head sees them: target row (b, j) is row b*(k+1)+j,
+ * drafter row (b, j) is row B*(k+1) + b*k + j (sample mode only; in draft mode
+ * drafter row (b, j) is row b*k + j). M_eff is the number of rows.
+ *   logits    [M_eff, V] fp32: the head's logits l = x . W^T.
+ *   probs     [M_eff, V] fp32: softmax(l / T) as the kernels normalise it.
+ *   argmax    [M_eff] int32: argmax of each row, lowest id on ties.
+ *   row_stats [M_eff, 2] fp64: {max_v l/T, sum_v exp(l/T - max)} per row.
+ *   pd_qd     [B, k, 2] fp64: {p_j(d_j), q_j(d_j)} of every slot (greedy: q = 0;
+ *             an out-of-range draft gives {-1, -1}).
+ */
+typedef struct mtpv_debug {
+    float* logits;
+    float* probs;
+    int32_t* argmax;
+    double* row_stats;
+    double* pd_qd;
+} mtpv_debug;
+
+/* Library version: major*10000 + minor*100 + patch. */
+MTPV_API int mtpv_version(void);
+
+/* Text for a status code (static storage; never NULL). */
+MTPV_API const char* mtpv_status_string(int status);
+
+/*
+ * Workspace bytes a call of the given mode and shape needs (0 if the shape is
+ * invalid). Host only; no GPU needed.
+ */
+MTPV_API size_t mtpv_workspace_bytes(int mode, int B, int k, int H, int V, int dtype);
+
+/*
+ * Host-only argument check shared by every call; returns what the call itself
+ * would return before enqueueing anything. Pointers are only checked for NULL
+ * and alignment, never dereferenced. For MTPV_MODE_DRAFT, k is the number of
+ * drafter rows per request, draft_hidden and draft_tokens (output) are
+ * required and target_hidden / accepted_len / out_tokens are ignored.
+ */
+MTPV_API int mtpv_check_args(int mode, int B, int k, int H, int V, int dtype, double temperature,
+                    const void* target_hidden, const void* draft_hidden, const void* W_lm,
+                    const int32_t* draft_tokens, const int32_t* accepted_len,
+                    const int32_t* out_tokens, const void* workspace, size_t workspace_bytes);
+
+/*
+ * Greedy verification.
+ * "The verifier accepts the longest prefix that agrees with the target model",
+ * so greedy speculative decoding returns exactly the tokens of ordinary greedy
+ * decoding ("The Tiny Draft Model Hidden Inside Qwen", section "How the draft
+ * becomes real output"). For each request b:
+ *   g_j = argmax_v l(target row j)  (lowest id on ties), j = 0..k
+ *   a   = number of leading slots with draft_tokens[b*k+j] == g_j  (0..k)
+ *   accepted_len[b] = a
+ *   out_tokens[b*(k+1) + j] = draft j for j < a, g_a for j = a, -1 after.
+ * hidden       [B, k+1, H] target hidden states (dtype)
+ * W_lm         [V, H] shared vocabulary head (dtype)
+ * draft_tokens [B, k] int32
+ * accepted_len [B] int32 (output), out_tokens [B, k+1] int32 (output)
+ * debug        NULL or exports (temperature 1 is used for probs / row_stats)
+ */
+MTPV_API int spec_verify_greedy(const void* hidden, const void* W_lm, const int32_t* draft_tokens,
+                       int B, int k, int H, int V, int dtype,
+                       int32_t* accepted_len, int32_t* out_tokens,
+                       void* workspace, size_t workspace_bytes,
+                       const mtpv_debug* debug, void* stream);
+
+/*
+ * Stochastic verification (exact speculative sampling).
+ * The surviving tokens must be distributed exactly as the target alone would
+ * produce them ("Speculative Decoding and MTP: Why Guessing Is Free", section
+ * "It's exact, not approximate"); the first rejected slot is replaced by a draw
+ * from the verifier's corrected distribution ("The Tiny Draft Model Hidden
+ * Inside Qwen", section "How the draft becomes real output"); k kept drafts
+ * give k+1 tokens ("Speculative Decoding and MTP: Why Guessing Is Free",
+ * section "Speculative decoding: draft, then verify"). The rule is the standard
+ * speculative-sampling rule (Leviathan, Kalman & Matias 2023; Chen et al. 2023):
+ *   u_j  = uniform(word 0 of Philox4x32-10(key = seed; counter = (j, b, offset)))
+ *   keep draft d = draft_tokens[b*k+j] iff u_j * q_j(d) < p_j(d)
+ *          (probability min(1, p/q)); a = first rejected slot, or k
+ *   a < k: out[a] ~ normalize(max(0, p_a - q_a)); a = k: out[k] ~ p_k (bonus);
+ *          the draw is the smallest id whose ascending prefix sum exceeds
+ *          u' * (total mass), u' = uniform(word 1 of the same Philox block at
+ *          slot a); if the residual mass is zero the draw uses p_a.
+ * uniform(x) = (x >> 8) * 2^-24. Philox key = (low 32 bits, high 32 bits) of
+ * seed; counter = (slot, request, low 32 bits, high 32 bits of offset).
+ * target_hidden [B, k+1, H], draft_hidden [B, k, H] (the drafter hidden states
+ * the drafts were sampled from), W_lm [V, H], draft_tokens [B, k].
+ * temperature > 0 applies to both p and q.
+ * Outputs as for spec_verify_greedy.
+ */
+MTPV_API int spec_verify_sample(const void* target_hidden, const void* draft_hidden, const void* W_lm,
+                       const int32_t* draft_tokens, int B, int k, int H, int V, int dtype,
+                       double temperature, uint64_t seed, uint64_t offset,
+                       int32_t* accepted_len, int32_t* out_tokens,
+                       void* workspace, size_t workspace_bytes,
+                       const mtpv_debug* debug, void* stream);
+
+/*
+ * Drafter-side sampling through the same shared head: for each request b and
+ * drafter row j (0..kd-1), draft_tokens[b*kd + j] ~ softmax(l(drafter row) / T),
+ * drawn by inverse transform with uniform(word 2 of Philox(seed; depth0 + j, b,
+ * offset)). The MTP module proposes tokens through the main model's head ("The
+ * Tiny Draft Model Hidden Inside Qwen", section "What vLLM and SGLang do with
+ * the weights"); a chained drafter calls this once per depth with kd = 1 and
+ * depth0 = depth, and the verify call then sees the same Philox stream.
+ * draft_hidden [B, kd, H]; draft_tokens [B, kd] int32 (output).
+ * Workspace: mtpv_workspace_bytes(MTPV_MODE_DRAFT, B, kd, H, V, dtype).
+ */
+MTPV_API int spec_draft_sample(const void* draft_hidden, const void* W_lm, int B, int kd, int depth0,
+                      int H, int V, int dtype, double temperature, uint64_t seed, uint64_t offset,
+                      int32_t* draft_tokens, void* workspace, size_t workspace_bytes,
+                      const mtpv_debug* debug, void* stream);
+
+/*
+ * Reads the device error word of the last call that used this workspace:
+ * waits for the stream, then copies the word to *err (0 = no error).
+ */
+MTPV_API int mtpv_device_error(const void* workspace, int32_t* err, void* stream);
+
+/*
+ * Measurement hooks. While enabled, every call records a pair of HIP events on
+ * its stream around the LM-head kernel (the kernel that streams W_lm). _read
+ * waits for those events and returns the summed kernel time in milliseconds and
+ * the number of timed launches, then clears them if reset != 0. At most 65536
+ * launches are kept between reads; later ones are not timed.
+ */
+MTPV_API int mtpv_timing_enable(int on);
+MTPV_API int mtpv_timing_read(double* ms_total, int64_t* launches, int reset);
+
+/*
+ * Plain device-to-device copy of `bytes` bytes with 16-byte vector loads and
+ * stores (bytes and both pointers 16-byte aligned). It is the reference kernel
+ * that scales hardware byte counters for traffic measurements.
+ */
+MTPV_API int mtpv_copy_bytes(void* dst, const void* src, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MTPV_H_ */

@@ -1,0 +1,387 @@
+// Host side of the C ABI declared in include/mtpv.h: argument checks, the
+// launch plan and workspace layout, the stream-ordered launch sequence, and the
+// measurement hooks.
+#include "mtpv.h"
+#include "mtpv_internal.h"
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <utility>
+#include <vector>
+
+namespace mtpv {
+
+namespace {
+
+constexpr int kMaxK = 64;
+constexpr int kLdsBudget = 64 * 1024;   // staging budget per workgroup (two workgroups fit per CU)
+constexpr double kLog2e = 1.442695040888963407359924681001892137;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int shape_status(int mode, int B, int k, int H, int V, int dtype) {
+    if (dtype != MTPV_BF16 && dtype != MTPV_F32) return MTPV_EDTYPE;
+    if (mode < MTPV_MODE_GREEDY || mode > MTPV_MODE_DRAFT) return MTPV_EINVAL;
+    if (B < 1 || B > (1 << 20) || k < 0 || k > kMaxK || H < 8 || H > (1 << 20) || V < 1 || V > (1 << 26))
+        return MTPV_EINVAL;
+    if (mode == MTPV_MODE_DRAFT && k < 1) return MTPV_EINVAL;
+    if (H % 8 != 0) return MTPV_EALIGN;
+    const long long meff = (long long)B * (k + 1) + (mode == MTPV_MODE_SAMPLE ? (long long)B * k : 0);
+    if (meff > (1 << 22)) return MTPV_EINVAL;
+    // sampling jobs and debug rows index the second grid dimension (at most 65535)
+    if (mode == MTPV_MODE_DRAFT && (long long)B * k > 65535) return MTPV_EINVAL;
+    if (meff > 65535) return MTPV_EINVAL;
+    return MTPV_OK;
+}
+
+}  // namespace
+
+int make_plan(int mode, int B, int k, int H, int V, int dtype, Plan* pl) {
+    const int st = shape_status(mode, B, k, H, V, dtype);
+    if (st != MTPV_OK) return st;
+    Plan p;
+    std::memset(&p, 0, sizeof(p));
+    p.mode = mode;
+    p.B = B;
+    p.k = k;
+    p.H = H;
+    p.V = V;
+    p.dtype = dtype;
+    p.es = dtype == MTPV_BF16 ? 2 : 4;
+    if (mode == MTPV_MODE_DRAFT) {
+        p.Mt = 0;
+        p.Meff = B * k;
+    } else {
+        p.Mt = B * (k + 1);
+        p.Meff = p.Mt + (mode == MTPV_MODE_SAMPLE ? B * k : 0);
+    }
+    // LM-head tile: positions in chunks of 16*nt, 16*va vocab rows per wave.
+    const int need = (p.Meff + 15) / 16;
+    if (p.es == 2) {
+        p.nt = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
+        p.va = p.nt == 1 ? 1 : 2;
+    } else {
+        p.va = 1;
+        p.nt = need <= 1 ? 1 : 2;
+    }
+    p.vblock = 64 * p.va;
+    p.S = (V + p.vblock - 1) / p.vblock;
+    p.MC = (p.Meff + 16 * p.nt - 1) / (16 * p.nt);
+    const int epv = 16 / p.es;
+    const int kstep = 4 * epv;
+    const int rows = std::min(16 * p.nt, p.Meff);
+    const int h_pad = (H + kstep - 1) / kstep * kstep;
+    int kc = ((kLdsBudget / rows - 16) / p.es) / kstep * kstep;
+    if (kc < kstep) kc = kstep;
+    p.kc = std::min(kc, h_pad);
+    const size_t stage = (size_t)rows * (p.kc * p.es + 16);
+    const size_t red = (size_t)4 * 16 * p.nt * sizeof(Partial);
+    p.lds = std::max(stage, red);
+    p.grid = p.MC == 1 ? p.S : ((p.S + 7) / 8) * 8 * p.MC;
+    // sampling jobs
+    p.ntiles = (V + 63) / 64;
+    p.NJ = mode == MTPV_MODE_GREEDY ? 0 : mode == MTPV_MODE_SAMPLE ? B : B * k;
+    if (p.NJ > 0) {
+        int c = (1024 + p.NJ - 1) / p.NJ;
+        c = std::max(1, std::min(c, 64));
+        p.C = std::min(c, p.ntiles);
+    }
+    // workspace layout
+    size_t off = 0;
+    p.off_err = off;
+    off = align_up(off + 4, 256);
+    p.off_partials = off;
+    off = align_up(off + (size_t)p.Meff * p.S * sizeof(Partial), 256);
+    p.off_dlogit = off;
+    off = align_up(off + (size_t)p.Meff * sizeof(float), 256);
+    p.off_rowstat = off;
+    off = align_up(off + (size_t)p.Meff * sizeof(RowStat), 256);
+    p.off_jobs = off;
+    off = align_up(off + (size_t)p.NJ * sizeof(Job), 256);
+    p.off_zpart = off;
+    off = align_up(off + (size_t)p.NJ * p.C * 2 * sizeof(double), 256);
+    p.off_tsum = off;
+    off = align_up(off + (size_t)p.NJ * p.ntiles * sizeof(double), 256);
+    p.off_spill = off;
+    if (mode != MTPV_MODE_GREEDY) off = align_up(off + (size_t)p.Meff * V * sizeof(float), 256);
+    p.total = off;
+    *pl = p;
+    return MTPV_OK;
+}
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// ------------------------------------------------------------- timing hooks
+struct Timing {
+    std::mutex mu;
+    bool on = false;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> events;
+    size_t used = 0;
+};
+
+Timing& timing() {
+    static Timing t;
+    return t;
+}
+
+constexpr size_t kMaxTimed = 65536;
+
+// Returns the event pair to record around this launch, or nullptr.
+std::pair<hipEvent_t, hipEvent_t>* timing_slot() {
+    Timing& t = timing();
+    std::lock_guard<std::mutex> lk(t.mu);
+    if (!t.on || t.used >= kMaxTimed) return nullptr;
+    if (t.used == t.events.size()) {
+        hipEvent_t a, b;
+        if (hipEventCreate(&a) != hipSuccess) return nullptr;
+        if (hipEventCreate(&b) != hipSuccess) {
+            (void)hipEventDestroy(a);
+            return nullptr;
+        }
+        t.events.emplace_back(a, b);
+    }
+    return &t.events[t.used++];
+}
+
+int common_check(int mode, int B, int k, int H, int V, int dtype, double temperature, const void* xt,
+                 const void* xd, const void* w, const int32_t* drafts, const int32_t* alen,
+                 const int32_t* out, const void* ws, size_t ws_bytes, Plan* plan) {
+    const int st = make_plan(mode, B, k, H, V, dtype, plan);
+    if (st != MTPV_OK) return st;
+    if (mode != MTPV_MODE_GREEDY && !(std::isfinite(temperature) && temperature > 0.0)) return MTPV_EINVAL;
+    if (w == nullptr) return MTPV_ENULL;
+    if (mode == MTPV_MODE_DRAFT) {
+        if (xd == nullptr || drafts == nullptr) return MTPV_ENULL;
+    } else {
+        if (xt == nullptr || alen == nullptr || out == nullptr) return MTPV_ENULL;
+        if (k > 0 && drafts == nullptr) return MTPV_ENULL;
+        if (mode == MTPV_MODE_SAMPLE && k > 0 && xd == nullptr) return MTPV_ENULL;
+    }
+    if (!aligned(w, 16) || (xt && !aligned(xt, 16)) || (xd && !aligned(xd, 16))) return MTPV_EALIGN;
+    if ((drafts && !aligned(drafts, 4)) || (alen && !aligned(alen, 4)) || (out && !aligned(out, 4)))
+        return MTPV_EALIGN;
+    if (ws == nullptr || !aligned(ws, 256) || ws_bytes < plan->total) return MTPV_EWORKSPACE;
+    return MTPV_OK;
+}
+
+int check_debug(const Plan& plan, const mtpv_debug* dbg) {
+    if (dbg == nullptr) return MTPV_OK;
+    if (dbg->logits && !aligned(dbg->logits, 16)) return MTPV_EALIGN;
+    if (dbg->probs && !dbg->logits && plan.mode == MTPV_MODE_GREEDY) return MTPV_EINVAL;
+    return MTPV_OK;
+}
+
+int run(const Plan& plan, const void* xt, const void* xd, const void* w, const int32_t* drafts,
+        double temperature, uint64_t seed, uint64_t offset, int depth0, int32_t* alen, int32_t* out,
+        void* ws, const mtpv_debug* dbg, hipStream_t stream) {
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    int32_t* err = reinterpret_cast<int32_t*>(base + plan.off_err);
+    Partial* partials = reinterpret_cast<Partial*>(base + plan.off_partials);
+    float* dlogit = reinterpret_cast<float*>(base + plan.off_dlogit);
+    RowStat* rowstat = reinterpret_cast<RowStat*>(base + plan.off_rowstat);
+    Job* jobs = reinterpret_cast<Job*>(base + plan.off_jobs);
+    double* zpart = reinterpret_cast<double*>(base + plan.off_zpart);
+    double* tsum = reinterpret_cast<double*>(base + plan.off_tsum);
+    float* spill = nullptr;
+    if (plan.mode != MTPV_MODE_GREEDY) spill = reinterpret_cast<float*>(base + plan.off_spill);
+    if (dbg && dbg->logits) spill = dbg->logits;
+
+    const double T = plan.mode == MTPV_MODE_GREEDY ? 1.0 : temperature;
+    const float c2f = (float)(kLog2e / T);
+
+    LmHeadArgs la;
+    la.xt = static_cast<const uint8_t*>(xt);
+    la.xd = static_cast<const uint8_t*>(xd);
+    la.w = static_cast<const uint8_t*>(w);
+    la.drafts = plan.mode == MTPV_MODE_DRAFT ? nullptr : drafts;
+    la.Mt = plan.Mt;
+    la.Meff = plan.Meff;
+    la.H = plan.H;
+    la.V = plan.V;
+    la.k = plan.k;
+    la.S = plan.S;
+    la.MC = plan.MC;
+    la.kc = plan.kc;
+    la.c2 = c2f;
+    la.partials = partials;
+    la.dlogit = dlogit;
+    la.spill = spill;
+    la.err = err;
+
+    std::pair<hipEvent_t, hipEvent_t>* ev = timing_slot();
+    if (ev && hipEventRecord(ev->first, stream) != hipSuccess) return MTPV_EDEVICE;
+    if (launch_lmhead(plan, la, stream) != hipSuccess) return MTPV_ELAUNCH;
+    if (ev && hipEventRecord(ev->second, stream) != hipSuccess) return MTPV_EDEVICE;
+
+    DecideArgs da;
+    da.partials = partials;
+    da.dlogit = dlogit;
+    da.drafts = plan.mode == MTPV_MODE_DRAFT ? nullptr : drafts;
+    da.mode = plan.mode;
+    da.B = plan.B;
+    da.k = plan.k;
+    da.V = plan.V;
+    da.Mt = plan.Mt;
+    da.Meff = plan.Meff;
+    da.S = plan.S;
+    da.depth0 = depth0;
+    da.c2f = c2f;
+    da.inv_t = 1.0 / T;
+    da.seed = seed;
+    da.offset = offset;
+    da.rowstat = rowstat;
+    da.accepted_len = alen;
+    da.out_tokens = out;
+    da.jobs = jobs;
+    da.err = err;
+    da.dbg_pdqd = (dbg && plan.mode != MTPV_MODE_DRAFT) ? dbg->pd_qd : nullptr;
+    da.dbg_argmax = dbg ? dbg->argmax : nullptr;
+    da.dbg_rowstats = dbg ? dbg->row_stats : nullptr;
+    if (launch_decide(plan, da, stream) != hipSuccess) return MTPV_ELAUNCH;
+
+    if (plan.NJ > 0) {
+        ResidualArgs ra;
+        ra.logits = spill;
+        ra.jobs = jobs;
+        ra.NJ = plan.NJ;
+        ra.V = plan.V;
+        ra.C = plan.C;
+        ra.ntiles = plan.ntiles;
+        ra.inv_t = 1.0 / T;
+        ra.zpart = zpart;
+        ra.tsum = tsum;
+        ra.out = plan.mode == MTPV_MODE_DRAFT ? const_cast<int32_t*>(drafts) : out;
+        if (launch_residual(plan, ra, stream) != hipSuccess) return MTPV_ELAUNCH;
+    }
+    if (dbg && dbg->probs) {
+        ProbsArgs pa;
+        pa.logits = spill;
+        pa.rowstat = rowstat;
+        pa.c2f = c2f;
+        pa.Meff = plan.Meff;
+        pa.V = plan.V;
+        pa.probs = dbg->probs;
+        if (launch_probs(pa, stream) != hipSuccess) return MTPV_ELAUNCH;
+    }
+    return MTPV_OK;
+}
+
+}  // namespace
+}  // namespace mtpv
+
+using namespace mtpv;
+
+extern "C" {
+
+int mtpv_version(void) { return 100; }
+
+const char* mtpv_status_string(int status) {
+    switch (status) {
+        case MTPV_OK: return "ok";
+        case MTPV_EINVAL: return "invalid size or scalar argument";
+        case MTPV_EALIGN: return "H not a multiple of 8 or pointer not 16-byte aligned";
+        case MTPV_EWORKSPACE: return "workspace missing, misaligned or too small";
+        case MTPV_EDTYPE: return "unknown dtype";
+        case MTPV_ENULL: return "required pointer is NULL";
+        case MTPV_ELAUNCH: return "kernel launch failed";
+        case MTPV_EDEVICE: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+size_t mtpv_workspace_bytes(int mode, int B, int k, int H, int V, int dtype) {
+    Plan p;
+    if (make_plan(mode, B, k, H, V, dtype, &p) != MTPV_OK) return 0;
+    return p.total;
+}
+
+int mtpv_check_args(int mode, int B, int k, int H, int V, int dtype, double temperature,
+                    const void* target_hidden, const void* draft_hidden, const void* W_lm,
+                    const int32_t* draft_tokens, const int32_t* accepted_len, const int32_t* out_tokens,
+                    const void* workspace, size_t workspace_bytes) {
+    Plan p;
+    return common_check(mode, B, k, H, V, dtype, temperature, target_hidden, draft_hidden, W_lm, draft_tokens,
+                        accepted_len, out_tokens, workspace, workspace_bytes, &p);
+}
+
+int spec_verify_greedy(const void* hidden, const void* W_lm, const int32_t* draft_tokens, int B, int k, int H,
+                       int V, int dtype, int32_t* accepted_len, int32_t* out_tokens, void* workspace,
+                       size_t workspace_bytes, const mtpv_debug* debug, void* stream) {
+    Plan p;
+    int st = common_check(MTPV_MODE_GREEDY, B, k, H, V, dtype, 1.0, hidden, nullptr, W_lm, draft_tokens,
+                          accepted_len, out_tokens, workspace, workspace_bytes, &p);
+    if (st == MTPV_OK) st = check_debug(p, debug);
+    if (st != MTPV_OK) return st;
+    return run(p, hidden, nullptr, W_lm, draft_tokens, 1.0, 0, 0, 0, accepted_len, out_tokens, workspace, debug,
+               static_cast<hipStream_t>(stream));
+}
+
+int spec_verify_sample(const void* target_hidden, const void* draft_hidden, const void* W_lm,
+                       const int32_t* draft_tokens, int B, int k, int H, int V, int dtype, double temperature,
+                       uint64_t seed, uint64_t offset, int32_t* accepted_len, int32_t* out_tokens,
+                       void* workspace, size_t workspace_bytes, const mtpv_debug* debug, void* stream) {
+    Plan p;
+    int st = common_check(MTPV_MODE_SAMPLE, B, k, H, V, dtype, temperature, target_hidden, draft_hidden, W_lm,
+                          draft_tokens, accepted_len, out_tokens, workspace, workspace_bytes, &p);
+    if (st == MTPV_OK) st = check_debug(p, debug);
+    if (st != MTPV_OK) return st;
+    return run(p, target_hidden, draft_hidden, W_lm, draft_tokens, temperature, seed, offset, 0, accepted_len,
+               out_tokens, workspace, debug, static_cast<hipStream_t>(stream));
+}
+
+int spec_draft_sample(const void* draft_hidden, const void* W_lm, int B, int kd, int depth0, int H, int V,
+                      int dtype, double temperature, uint64_t seed, uint64_t offset, int32_t* draft_tokens,
+                      void* workspace, size_t workspace_bytes, const mtpv_debug* debug, void* stream) {
+    Plan p;
+    if (depth0 < 0) return MTPV_EINVAL;
+    int st = common_check(MTPV_MODE_DRAFT, B, kd, H, V, dtype, temperature, nullptr, draft_hidden, W_lm,
+                          draft_tokens, nullptr, nullptr, workspace, workspace_bytes, &p);
+    if (st == MTPV_OK) st = check_debug(p, debug);
+    if (st != MTPV_OK) return st;
+    return run(p, nullptr, draft_hidden, W_lm, draft_tokens, temperature, seed, offset, depth0, nullptr, nullptr,
+               workspace, debug, static_cast<hipStream_t>(stream));
+}
+
+int mtpv_device_error(const void* workspace, int32_t* err, void* stream) {
+    if (workspace == nullptr || err == nullptr) return MTPV_ENULL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (hipStreamSynchronize(s) != hipSuccess) return MTPV_EDEVICE;
+    if (hipMemcpy(err, workspace, sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess) return MTPV_EDEVICE;
+    return MTPV_OK;
+}
+
+int mtpv_timing_enable(int on) {
+    Timing& t = timing();
+    std::lock_guard<std::mutex> lk(t.mu);
+    t.on = on != 0;
+    return MTPV_OK;
+}
+
+int mtpv_timing_read(double* ms_total, int64_t* launches, int reset) {
+    if (ms_total == nullptr || launches == nullptr) return MTPV_ENULL;
+    Timing& t = timing();
+    std::lock_guard<std::mutex> lk(t.mu);
+    double total = 0.0;
+    for (size_t i = 0; i < t.used; ++i) {
+        if (hipEventSynchronize(t.events[i].second) != hipSuccess) return MTPV_EDEVICE;
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, t.events[i].first, t.events[i].second) != hipSuccess) return MTPV_EDEVICE;
+        total += ms;
+    }
+    *ms_total = total;
+    *launches = (int64_t)t.used;
+    if (reset) t.used = 0;
+    return MTPV_OK;
+}
+
+int mtpv_copy_bytes(void* dst, const void* src, size_t bytes, void* stream) {
+    if (dst == nullptr || src == nullptr) return MTPV_ENULL;
+    if (!aligned(dst, 16) || !aligned(src, 16) || bytes % 16 != 0) return MTPV_EALIGN;
+    if (launch_copy(dst, src, bytes, static_cast<hipStream_t>(stream)) != hipSuccess) return MTPV_ELAUNCH;
+    return MTPV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,124 @@
+// Internal declarations shared by the host API (api.hip) and the kernel files.
+// Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mtpv {
+
+// Per-(row, vocab block) statistics written by the LM-head kernel's epilogue.
+//   x  = max over the block of l * c2 (c2 = log2(e) / T, fp32), i.e. log2 units
+//   s  = sum over the block of exp2(l * c2 - x)
+//   bv = largest raw logit in the block, bi = its lowest vocabulary id
+struct Partial {
+    float x;
+    float s;
+    float bv;
+    int bi;
+};
+
+// Per-row statistics after combining every vocab block (fixed order).
+struct RowStat {
+    double x;   // max of l * c2 (log2 units)
+    double z;   // sum of exp2(l * c2 - x)
+    float bv;   // max raw logit
+    int bi;     // its lowest id
+    int pad[2];
+};
+
+// One inverse-CDF draw: from normalize(max(0, p - q)) when row_q >= 0, else from p.
+struct Job {
+    int row_p;      // row of the spilled logits giving p
+    int row_q;      // row giving q, or -1
+    int out_index;  // element of the output token array to write
+    int pad;
+    double u;       // uniform in [0, 1)
+    double ref_p;   // reference (about the row max of l / T) for the fp64 exponentials
+    double ref_q;
+};
+
+struct Plan {
+    int mode, B, k, H, V, dtype;
+    int es;          // element size (2 for bf16, 4 for fp32)
+    int Mt, Meff;    // target rows, all rows the head sees
+    int va, nt;      // LM-head kernel tile: 16*va vocab rows per wave, 16*nt rows per M chunk
+    int vblock;      // vocab rows per workgroup (64 * va)
+    int S;           // vocab blocks
+    int MC;          // M chunks
+    int kc;          // hidden elements staged per LDS pass
+    size_t lds;      // dynamic LDS bytes of the LM-head kernel
+    int grid;        // LM-head workgroups (1-D, XCD-aware ordering when MC > 1)
+    int NJ;          // inverse-CDF jobs (0 in greedy mode)
+    int C;           // chunks per job in the residual passes
+    int ntiles;      // 64-element tiles per vocabulary row
+    // workspace layout (byte offsets)
+    size_t off_err, off_partials, off_dlogit, off_rowstat, off_jobs, off_zpart, off_tsum, off_spill;
+    size_t total;
+};
+
+// Returns 0 and fills *plan, or a negative status for an invalid shape.
+int make_plan(int mode, int B, int k, int H, int V, int dtype, Plan* plan);
+
+struct LmHeadArgs {
+    const uint8_t* xt;      // target rows [Mt, H]
+    const uint8_t* xd;      // drafter rows [Meff - Mt, H]
+    const uint8_t* w;       // head [V, H]
+    const int32_t* drafts;  // [B, k] or NULL (draft mode)
+    int Mt, Meff, H, V, k;
+    int S, MC, kc;
+    float c2;               // log2(e) / T
+    Partial* partials;      // [Meff, S]
+    float* dlogit;          // [Meff]
+    float* spill;           // [Meff, V] or NULL
+    int32_t* err;           // cleared by the first workgroup
+};
+
+hipError_t launch_lmhead(const Plan& plan, const LmHeadArgs& args, hipStream_t stream);
+
+struct DecideArgs {
+    const Partial* partials;
+    const float* dlogit;
+    const int32_t* drafts;  // [B, k] (greedy, sample)
+    int mode, B, k, V, Mt, Meff, S, depth0;
+    float c2f;              // the fp32 constant the epilogue used
+    double inv_t;           // 1 / T in fp64
+    uint64_t seed, offset;
+    RowStat* rowstat;       // [Meff]
+    int32_t* accepted_len;  // [B]
+    int32_t* out_tokens;    // [B, k+1] (greedy, sample) or [B, k] (draft)
+    Job* jobs;              // [NJ]
+    int32_t* err;
+    double* dbg_pdqd;       // [B, k, 2] or NULL
+    int32_t* dbg_argmax;    // [Meff] or NULL
+    double* dbg_rowstats;   // [Meff, 2] or NULL
+};
+
+hipError_t launch_decide(const Plan& plan, const DecideArgs& args, hipStream_t stream);
+
+struct ResidualArgs {
+    const float* logits;    // spilled logits [Meff, V]
+    const Job* jobs;
+    int NJ, V, C, ntiles;
+    double inv_t;
+    double* zpart;          // [NJ, C, 2]
+    double* tsum;           // [NJ, ntiles]
+    int32_t* out;           // token output array (indexed by Job::out_index)
+};
+
+hipError_t launch_residual(const Plan& plan, const ResidualArgs& args, hipStream_t stream);
+
+struct ProbsArgs {
+    const float* logits;
+    const RowStat* rowstat;
+    float c2f;
+    int Meff, V;
+    float* probs;
+};
+
+hipError_t launch_probs(const ProbsArgs& args, hipStream_t stream);
+
+hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
+}  // namespace mtpv

@@ -1,0 +1,459 @@
+// Cross-block combine, acceptance decisions, longest-prefix scan and the fp64
+// inverse-CDF sampler of the verify step.
+//
+// decide_kernel (one workgroup per request) merges the LM-head kernel's
+// per-(row, vocab block) partials in a fixed order into per-row {max, sum of
+// exp, argmax}, takes the acceptance decisions slot by slot and scans for the
+// first rejection ("accept the longest correct prefix", "Speculative Decoding
+// and MTP: Why Guessing Is Free", section "Speculative decoding: draft, then
+// verify"; "The Tiny Draft Model Hidden Inside Qwen", section "How the draft
+// becomes real output"), writes accepted_len / out_tokens and, when a token
+// must be drawn, one sampling job.
+//
+// The draw itself (correction from normalize(max(0, p - q)) at the first
+// rejection, bonus from p_k after k acceptances, or a drafter draw from q)
+// runs in fp64 over the spilled fp32 logits in three passes over the one or two
+// rows a job needs: per-chunk sums of exp(l/T - ref) (the normaliser, in fp64,
+// recomputed here with the exact 1/T), per-64-token tile sums of the weights,
+// and a search over those sums in a fixed order followed by a wave-level scan
+// inside the chosen tile. Every comparison uses sums built in one fixed order,
+// so the search is consistent and bit-reproducible.
+#include "mtpv_internal.h"
+
+#include <climits>
+
+namespace mtpv {
+namespace {
+
+constexpr double kLn2 = 0.693147180559945309417232121458176568;
+
+// ---------------------------------------------------------------- Philox4x32-10
+// Salmon, Moraes, Dror & Shaw, SC'11: ten rounds over a 4-word counter with a
+// 2-word key bumped by two Weyl constants between rounds.
+__device__ __forceinline__ void philox_block(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                             uint32_t k0, uint32_t k1, uint32_t out[4]) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint32_t hi0 = __umulhi(0xD2511F53u, c0);
+        const uint32_t lo0 = 0xD2511F53u * c0;
+        const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2);
+        const uint32_t lo1 = 0xCD9E8D57u * c2;
+        const uint32_t n0 = hi1 ^ c1 ^ k0;
+        const uint32_t n2 = hi0 ^ c3 ^ k1;
+        c0 = n0;
+        c1 = lo1;
+        c2 = n2;
+        c3 = lo0;
+    }
+    out[0] = c0;
+    out[1] = c1;
+    out[2] = c2;
+    out[3] = c3;
+}
+
+// Uniform on the 24-bit grid: (x >> 8) * 2^-24, exact in fp64.
+__device__ __forceinline__ double uniform24(uint32_t x) { return (double)(x >> 8) * 0x1p-24; }
+
+// Word `word` of Philox(key = seed; counter = (slot, request, offset lo, offset hi)).
+__device__ __forceinline__ double slot_uniform(uint64_t seed, uint64_t offset, int slot, int req, int word) {
+    uint32_t o[4];
+    philox_block((uint32_t)slot, (uint32_t)req, (uint32_t)offset, (uint32_t)(offset >> 32), (uint32_t)seed,
+                 (uint32_t)(seed >> 32), o);
+    return uniform24(o[word]);
+}
+
+// ------------------------------------------------------------ row combination
+struct Acc {
+    double x;
+    double z;
+    float bv;
+    int bi;
+};
+
+__device__ __forceinline__ Acc acc_merge(Acc a, Acc b) {
+    const double ninf = -__builtin_inf();
+    Acc o;
+    o.x = fmax(a.x, b.x);
+    const double za = (a.x == ninf) ? 0.0 : a.z * exp2(a.x - o.x);
+    const double zb = (b.x == ninf) ? 0.0 : b.z * exp2(b.x - o.x);
+    o.z = za + zb;
+    const bool take_b = (b.bv > a.bv) || (b.bv == a.bv && b.bi < a.bi);
+    o.bv = take_b ? b.bv : a.bv;
+    o.bi = take_b ? b.bi : a.bi;
+    return o;
+}
+
+__device__ __forceinline__ Acc acc_shfl_xor(Acc a, int off) {
+    Acc o;
+    o.x = __shfl_xor(a.x, off);
+    o.z = __shfl_xor(a.z, off);
+    o.bv = __shfl_xor(a.bv, off);
+    o.bi = __shfl_xor(a.bi, off);
+    return o;
+}
+
+// Block-wide fixed-order combine of row r's S partials; the result is valid in thread 0.
+__device__ Acc combine_row(const Partial* partials, int S, int r, Acc* sh) {
+    const int tid = threadIdx.x;
+    Acc a{-__builtin_inf(), 0.0, -__builtin_inff(), INT_MAX};
+    const Partial* row = partials + (size_t)r * S;
+    for (int s = tid; s < S; s += 256) {
+        const Partial q = row[s];
+        a = acc_merge(a, Acc{(double)q.x, (double)q.s, q.bv, q.bi});
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) a = acc_merge(a, acc_shfl_xor(a, off));
+    if ((tid & 63) == 0) sh[tid >> 6] = a;
+    __syncthreads();
+    Acc o = sh[0];
+    if (tid == 0) {
+        for (int w = 1; w < 4; ++w) o = acc_merge(o, sh[w]);
+    }
+    __syncthreads();
+    return o;
+}
+
+__global__ __launch_bounds__(256) void decide_kernel(DecideArgs p) {
+    __shared__ Acc sh[4];
+    __shared__ RowStat rows[129];
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int k = p.k;
+    // rows of this request, in the order: target 0..k (greedy / sample), drafter 0..k-1 (sample)
+    // draft mode: drafter rows 0..k-1 only
+    int nrows;
+    if (p.mode == 0) nrows = k + 1;
+    else if (p.mode == 1) nrows = 2 * k + 1;
+    else nrows = k;
+    for (int i = 0; i < nrows; ++i) {
+        int r;
+        if (p.mode == 2) r = b * k + i;
+        else if (i <= k) r = b * (k + 1) + i;
+        else r = p.Mt + b * k + (i - k - 1);
+        const Acc a = combine_row(p.partials, p.S, r, sh);
+        if (tid == 0) {
+            RowStat rs;
+            rs.x = a.x;
+            rs.z = a.z;
+            rs.bv = a.bv;
+            rs.bi = a.bi;
+            rs.pad[0] = rs.pad[1] = 0;
+            rows[i] = rs;
+            p.rowstat[r] = rs;
+            if (p.dbg_argmax) p.dbg_argmax[r] = a.bi;
+            if (p.dbg_rowstats) {
+                p.dbg_rowstats[2 * r] = a.x * kLn2;
+                p.dbg_rowstats[2 * r + 1] = a.z;
+            }
+        }
+    }
+    __syncthreads();
+    if (tid != 0) return;
+
+    if (p.mode == 2) {
+        for (int j = 0; j < k; ++j) {
+            const int r = b * k + j;
+            Job job;
+            job.row_p = r;
+            job.row_q = -1;
+            job.out_index = r;
+            job.pad = 0;
+            job.u = slot_uniform(p.seed, p.offset, p.depth0 + j, b, 2);
+            job.ref_p = rows[j].x * kLn2;
+            job.ref_q = 0.0;
+            p.jobs[r] = job;
+        }
+        return;
+    }
+
+    int a = k;
+    for (int j = 0; j < k; ++j) {
+        const int d = p.drafts[b * k + j];
+        const bool in_range = d >= 0 && d < p.V;
+        if (!in_range) atomicOr(p.err, 1);
+        const int rt = b * (k + 1) + j;
+        double pj = -1.0, qj = -1.0;
+        bool keep = false;
+        if (in_range) {
+            const RowStat& st = rows[j];
+            pj = exp2((double)(p.dlogit[rt] * p.c2f) - st.x) / st.z;
+            if (p.mode == 0) {
+                qj = 0.0;
+                keep = (d == st.bi);
+            } else {
+                const int rd = p.Mt + b * k + j;
+                const RowStat& sd = rows[k + 1 + j];
+                qj = exp2((double)(p.dlogit[rd] * p.c2f) - sd.x) / sd.z;
+                const double u = slot_uniform(p.seed, p.offset, j, b, 0);
+                keep = u * qj < pj;
+            }
+        }
+        if (p.dbg_pdqd) {
+            p.dbg_pdqd[2 * (b * k + j)] = pj;
+            p.dbg_pdqd[2 * (b * k + j) + 1] = qj;
+        }
+        if (a == k && !keep) a = j;
+    }
+    p.accepted_len[b] = a;
+    int32_t* out = p.out_tokens + (size_t)b * (k + 1);
+    for (int j = 0; j <= k; ++j) {
+        int t = -1;
+        if (j < a) t = p.drafts[b * k + j];
+        else if (j == a && p.mode == 0) t = rows[a].bi;
+        out[j] = t;
+    }
+    if (p.mode == 1) {
+        Job job;
+        job.row_p = b * (k + 1) + a;
+        job.row_q = (a < k) ? p.Mt + b * k + a : -1;
+        job.out_index = b * (k + 1) + a;
+        job.pad = 0;
+        job.u = slot_uniform(p.seed, p.offset, a, b, 1);
+        job.ref_p = rows[a].x * kLn2;
+        job.ref_q = (a < k) ? rows[k + 1 + a].x * kLn2 : 0.0;
+        p.jobs[b] = job;
+    }
+}
+
+// ------------------------------------------------------------ sampling passes
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+// exp(l / T - ref) in fp64 for element v of `row` (0 past V or for row < 0).
+__device__ __forceinline__ double row_exp(const float* logits, int row, int V, int v, double inv_t, double ref) {
+    if (row < 0 || v >= V) return 0.0;
+    const double l = (double)logits[(size_t)row * V + v];
+    return exp(fma(l, inv_t, -ref));
+}
+
+// Weight of element v for a job: max(0, p - q) with a drafter row, else p.
+__device__ __forceinline__ double job_weight(const float* logits, const Job& job, bool use_q, int V, int v,
+                                             double inv_t, double zp, double zq) {
+    const double pv = row_exp(logits, job.row_p, V, v, inv_t, job.ref_p) / zp;
+    if (!use_q) return pv;
+    const double qv = row_exp(logits, job.row_q, V, v, inv_t, job.ref_q) / zq;
+    const double d = pv - qv;
+    return d > 0.0 ? d : 0.0;
+}
+
+// Inclusive scan over one 64-token tile, lane i holding token tile*64 + i.
+__device__ __forceinline__ double tile_scan(const float* logits, const Job& job, bool use_q, int V, int tile,
+                                            double inv_t, double zp, double zq, int lane) {
+    double x = job_weight(logits, job, use_q, V, tile * 64 + lane, inv_t, zp, zq);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const double y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+__device__ __forceinline__ void normalisers(const ResidualArgs& p, int j, double* zp, double* zq) {
+    double a = 0.0, b = 0.0;
+    const double* zpart = p.zpart + (size_t)j * p.C * 2;
+    for (int c = 0; c < p.C; ++c) {
+        a += zpart[2 * c];
+        b += zpart[2 * c + 1];
+    }
+    *zp = a;
+    *zq = b;
+}
+
+// Pass 1: per-chunk sums of exp(l/T - ref) for the job's p row and q row.
+__global__ __launch_bounds__(256) void zsum_kernel(ResidualArgs p) {
+    __shared__ double sh[2][4];
+    const int j = blockIdx.y, c = blockIdx.x;
+    const Job job = p.jobs[j];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tpc = (p.ntiles + p.C - 1) / p.C;
+    const int t0 = c * tpc, t1 = min(p.ntiles, t0 + tpc);
+    double sp = 0.0, sq = 0.0;
+    for (int t = t0 + wave; t < t1; t += 4) {
+        const int v = t * 64 + lane;
+        sp += row_exp(p.logits, job.row_p, p.V, v, p.inv_t, job.ref_p);
+        sq += row_exp(p.logits, job.row_q, p.V, v, p.inv_t, job.ref_q);
+    }
+    sp = wave_sum(sp);
+    sq = wave_sum(sq);
+    if (lane == 0) {
+        sh[0][wave] = sp;
+        sh[1][wave] = sq;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double* out = p.zpart + ((size_t)j * p.C + c) * 2;
+        out[0] = ((sh[0][0] + sh[0][1]) + sh[0][2]) + sh[0][3];
+        out[1] = ((sh[1][0] + sh[1][1]) + sh[1][2]) + sh[1][3];
+    }
+}
+
+// Pass 2: per-tile sums of the job's weights.
+__global__ __launch_bounds__(256) void tsum_kernel(ResidualArgs p) {
+    const int j = blockIdx.y, c = blockIdx.x;
+    const Job job = p.jobs[j];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    double zp, zq;
+    normalisers(p, j, &zp, &zq);
+    const bool use_q = job.row_q >= 0;
+    const int tpc = (p.ntiles + p.C - 1) / p.C;
+    const int t0 = c * tpc, t1 = min(p.ntiles, t0 + tpc);
+    for (int t = t0 + wave; t < t1; t += 4) {
+        const double incl = tile_scan(p.logits, job, use_q, p.V, t, p.inv_t, zp, zq, lane);
+        if (lane == 63) p.tsum[(size_t)j * p.ntiles + t] = incl;
+    }
+}
+
+// Pass 3: locate u * (total weight) in the fixed-order sums and emit the token.
+__global__ __launch_bounds__(256) void search_kernel(ResidualArgs p) {
+    __shared__ double thread_tot[256];
+    __shared__ int sh_tile;
+    __shared__ double sh_base;
+    __shared__ double sh_target;
+    __shared__ int sh_retry;
+    const int j = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const Job job = p.jobs[j];
+    double zp, zq;
+    normalisers(p, j, &zp, &zq);
+    bool use_q = job.row_q >= 0;
+    double* ts = p.tsum + (size_t)j * p.ntiles;
+    const int per = (p.ntiles + 255) / 256;
+
+    for (int pass = 0; pass < 2; ++pass) {
+        if (pass == 1) {
+            // Residual mass was zero: draw from p instead (tile sums rebuilt for p).
+            for (int t = wave; t < p.ntiles; t += 4) {
+                const double incl = tile_scan(p.logits, job, false, p.V, t, p.inv_t, zp, zq, lane);
+                if (lane == 63) ts[t] = incl;
+            }
+            __syncthreads();
+        }
+        double tot = 0.0;
+        for (int i = tid * per; i < min(p.ntiles, (tid + 1) * per); ++i) tot += ts[i];
+        thread_tot[tid] = tot;
+        __syncthreads();
+        if (tid == 0) {
+            double R = 0.0;
+            for (int t = 0; t < 256; ++t) R += thread_tot[t];
+            sh_retry = 0;
+            if (!(R > 0.0)) {
+                sh_retry = (pass == 0 && use_q) ? 1 : 0;
+                sh_tile = 0;
+                sh_base = 0.0;
+                sh_target = -1.0;  // degenerate: every weight is zero; take token 0
+            } else {
+                // Skip whole thread ranges while their fixed-order totals stay at or
+                // below the target, then walk tiles one by one from there. The walk may
+                // run past that range: a range total and the running sum of its tiles
+                // associate differently and can differ in the last bit.
+                const double target = job.u * R;
+                double run = 0.0;
+                int tt = -1;
+                for (int t = 0; t < 256; ++t) {
+                    if (run + thread_tot[t] > target) {
+                        tt = t;
+                        break;
+                    }
+                    run += thread_tot[t];
+                }
+                if (tt < 0) {
+                    tt = 0;
+                    run = 0.0;
+                }
+                int found = -1;
+                for (int i = tt * per; i < p.ntiles; ++i) {
+                    if (run + ts[i] > target) {
+                        found = i;
+                        break;
+                    }
+                    run += ts[i];
+                }
+                if (found < 0) {  // rounding put the target past the end: last tile with mass
+                    int last = 0;
+                    for (int i = 0; i < p.ntiles; ++i)
+                        if (ts[i] > 0.0) last = i;
+                    run = 0.0;
+                    for (int i = 0; i < last; ++i) run += ts[i];
+                    found = last;
+                }
+                sh_tile = found;
+                sh_base = run;
+                sh_target = target;
+            }
+        }
+        __syncthreads();
+        if (sh_retry) {
+            use_q = false;
+            __syncthreads();
+            continue;
+        }
+        if (wave == 0) {
+            const double incl = tile_scan(p.logits, job, use_q, p.V, sh_tile, p.inv_t, zp, zq, lane);
+            const double w = job_weight(p.logits, job, use_q, p.V, sh_tile * 64 + lane, p.inv_t, zp, zq);
+            const unsigned long long hit = __ballot(sh_base + incl > sh_target);
+            const unsigned long long pos = __ballot(w > 0.0);
+            int ln;
+            if (hit) ln = __ffsll(hit) - 1;
+            else if (pos) ln = 63 - __clzll(pos);
+            else ln = 0;
+            if (lane == 0) p.out[job.out_index] = min(sh_tile * 64 + ln, p.V - 1);
+        }
+        break;
+    }
+}
+
+// Debug export: probs[r][v] = exp2(l * c2 - x_r) / z_r with the kernels' own row statistics.
+__global__ __launch_bounds__(256) void probs_kernel(ProbsArgs p) {
+    const int r = blockIdx.y;
+    const int v = blockIdx.x * 256 + threadIdx.x;
+    if (v >= p.V) return;
+    const RowStat st = p.rowstat[r];
+    const float l = p.logits[(size_t)r * p.V + v];
+    p.probs[(size_t)r * p.V + v] = (float)(exp2((double)(l * p.c2f) - st.x) / st.z);
+}
+
+__global__ __launch_bounds__(256) void copy_kernel(uint4* __restrict__ dst, const uint4* __restrict__ src, size_t n) {
+    const size_t stride = (size_t)gridDim.x * 256;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) dst[i] = src[i];
+}
+
+}  // namespace
+
+hipError_t launch_decide(const Plan& plan, const DecideArgs& args, hipStream_t stream) {
+    hipLaunchKernelGGL(decide_kernel, dim3(plan.B), dim3(256), 0, stream, args);
+    return hipGetLastError();
+}
+
+hipError_t launch_residual(const Plan& plan, const ResidualArgs& args, hipStream_t stream) {
+    hipLaunchKernelGGL(zsum_kernel, dim3(args.C, args.NJ), dim3(256), 0, stream, args);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(tsum_kernel, dim3(args.C, args.NJ), dim3(256), 0, stream, args);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(search_kernel, dim3(args.NJ), dim3(256), 0, stream, args);
+    return hipGetLastError();
+}
+
+hipError_t launch_probs(const ProbsArgs& args, hipStream_t stream) {
+    hipLaunchKernelGGL(probs_kernel, dim3((args.V + 255) / 256, args.Meff), dim3(256), 0, stream, args);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+    const size_t n = bytes / 16;
+    const unsigned grid = (unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(copy_kernel, dim3(grid), dim3(256), 0, stream, (uint4*)dst, (const uint4*)src, n);
+    return hipGetLastError();
+}
+
+}  // namespace mtpv

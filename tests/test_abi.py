@@ -1,0 +1,113 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol include/mtpv.h
+declares, sizes workspaces, and its host-side validation returns each error code.
+No compute call is made here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mtp_draft_verification_amd as mv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mtpv.h")
+
+# synthetic, well-aligned fake device addresses: validation never dereferences them
+A = 0x10000
+WS = 0x200000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"MTPV_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = mv.lib()
+    names = declared_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(mv.EXPORTED)
+    assert L.mtpv_version() >= 100
+
+
+def test_status_strings():
+    for code in mv.STATUS:
+        s = mv.status_string(code)
+        assert isinstance(s, str) and s
+    assert mv.status_string(12345) == "unknown status"
+
+
+def ws_bytes(mode=0, B=2, k=3, H=256, V=1000, dtype=0):
+    return mv.workspace_bytes(mode, B, k, H, V, dtype)
+
+
+def test_workspace_sizes():
+    g = ws_bytes(0)
+    s = ws_bytes(1)
+    d = ws_bytes(2)
+    assert g > 0 and s > g and d > 0
+    # sample mode holds the fp32 logit spill for all target and drafter rows
+    assert s >= (2 * 4 + 2 * 3) * 1000 * 4
+    assert ws_bytes(0, V=0) == 0 and ws_bytes(0, H=12) == 0 and ws_bytes(5) == 0
+    assert ws_bytes(2, k=0) == 0
+    # full-size shapes fit comfortably in one GPU's HBM
+    assert mv.workspace_bytes(1, 256, 3, 7168, 129280, 0) < 2 << 30
+
+
+def check(**kw):
+    args = dict(mode=0, B=2, k=3, H=256, V=1000, dtype=0, temperature=1.0, target_hidden=A, draft_hidden=A,
+                W=A, drafts=A, accepted_len=A, out_tokens=A, workspace=WS, ws_bytes=None)
+    args.update(kw)
+    if args["ws_bytes"] is None:
+        args["ws_bytes"] = max(1, ws_bytes(max(0, min(2, args["mode"])), max(1, args["B"]), max(0, args["k"]),
+                                           args["H"] if args["H"] % 8 == 0 and args["H"] >= 8 else 256,
+                                           max(1, args["V"]), 0))
+    return mv.check_args(args["mode"], args["B"], args["k"], args["H"], args["V"], args["dtype"],
+                         args["temperature"], args["target_hidden"], args["draft_hidden"], args["W"],
+                         args["drafts"], args["accepted_len"], args["out_tokens"], args["workspace"],
+                         args["ws_bytes"])
+
+
+def test_valid_arguments_pass():
+    assert check() == 0
+    assert check(mode=1, temperature=0.7) == 0
+    assert check(mode=2, target_hidden=None, accepted_len=None, out_tokens=None) == 0
+    assert check(k=0, drafts=None) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), -1), (dict(k=-1), -1), (dict(k=65), -1), (dict(V=0), -1), (dict(H=0), -1),
+    (dict(mode=7), -1), (dict(mode=1, temperature=0.0), -1), (dict(mode=1, temperature=float("nan")), -1),
+    (dict(mode=1, temperature=-1.0), -1), (dict(mode=2, k=0), -1),
+    (dict(H=260), -2), (dict(W=A + 8), -2), (dict(target_hidden=A + 4), -2), (dict(drafts=A + 2), -2),
+    (dict(workspace=None), -3), (dict(workspace=WS + 64), -3), (dict(ws_bytes=16), -3),
+    (dict(dtype=2), -4), (dict(dtype=-1), -4),
+    (dict(W=None), -5), (dict(target_hidden=None), -5), (dict(drafts=None), -5),
+    (dict(accepted_len=None), -5), (dict(out_tokens=None), -5),
+    (dict(mode=1, draft_hidden=None), -5), (dict(mode=2, draft_hidden=None), -5),
+])
+def test_each_error_code(kw, code):
+    assert check(**kw) == code
+
+
+def test_greedy_ignores_temperature():
+    assert check(temperature=0.0) == 0
+
+
+def test_calls_reject_bad_arguments_before_touching_the_device():
+    """The compute entry points validate on the host first: with invalid sizes they
+    return the error without enqueueing anything (so this runs without a GPU)."""
+    L = mv.lib()
+    st = L.spec_verify_greedy(ctypes.c_void_p(A), ctypes.c_void_p(A), ctypes.c_void_p(A), 0, 3, 256, 1000, 0,
+                              ctypes.c_void_p(A), ctypes.c_void_p(A), ctypes.c_void_p(WS), 1 << 20, None, None)
+    assert st == -1
+    st = L.spec_verify_sample(ctypes.c_void_p(A), ctypes.c_void_p(A), ctypes.c_void_p(A), ctypes.c_void_p(A), 2,
+                              3, 256, 1000, 0, -1.0, 0, 0, ctypes.c_void_p(A), ctypes.c_void_p(A),
+                              ctypes.c_void_p(WS), 1 << 30, None, None)
+    assert st == -1
+    st = L.spec_draft_sample(ctypes.c_void_p(A), ctypes.c_void_p(A), 2, 3, -1, 256, 1000, 0, 1.0, 0, 0,
+                             ctypes.c_void_p(A), ctypes.c_void_p(WS), 1 << 30, None, None)
+    assert st == -1
+    assert L.mtpv_copy_bytes(ctypes.c_void_p(A), ctypes.c_void_p(A + 4), 16, None) == -2

@@ -1,0 +1,159 @@
+"""GPU parity of the HIP verify path against the CPU oracle, through the C ABI.
+
+Small shapes span several vocabulary tiles, ragged vocabulary and hidden tails,
+several position chunks and hidden chunks, k = 0 and k up to 8, both dtypes; they
+are compared element by element (logits, probabilities, argmax, accepted lengths,
+emitted tokens). Edge cases: out-of-range draft ids, drafts equal to the target
+argmax, drafter rows equal to target rows, determinism, the drafter call.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mtp_draft_verification_amd as mv
+import oracle
+import synth
+from gpu_util import (EXCUSE_RATE, Case, check_invariants, check_numerics, compare_outcomes, dev, gpu_run,
+                      load_workload, oracle_run, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+C = synth.custom
+SMALL = {
+    "cfg1_tiny_f32": (synth.CONFIGS[1], 60),
+    "ragged_vocab_bf16": (C(H=512, V=5000, B=3, k=3, T=0.8, cid=101), 12),
+    "ragged_hidden_bf16": (C(H=264, V=1000, B=2, k=2, cid=102), 12),
+    "position_chunks_bf16": (C(H=256, V=3000, B=40, k=3, T=0.9, cid=103), 3),
+    "hidden_chunks_bf16": (C(H=1024, V=2048, B=32, k=3, cid=104), 3),
+    "k0_bf16": (C(H=256, V=777, B=5, k=0, cid=105), 8),
+    "B1_k1_bf16": (C(H=128, V=64, B=1, k=1, cid=106), 20),
+    "k8_f32": (C(H=64, V=300, B=2, k=8, dtype="f32", cid=107), 12),
+    "V50_bf16": (C(H=64, V=50, B=3, k=2, cid=108), 12),
+    "position_chunks_f32": (C(H=128, V=500, B=8, k=3, dtype="f32", cid=109), 6),
+}
+
+
+@pytest.fixture(scope="module")
+def weights_cache():
+    return {}
+
+
+def _weights(cache, wl):
+    if wl.cid not in cache:
+        W_store, W64 = load_workload(wl)
+        cache[wl.cid] = (W_store, W64, to_dev(W_store, wl.dtype))
+    return cache[wl.cid]
+
+
+@pytest.mark.parametrize("mode", ["greedy", "sample"])
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_parity(name, mode, weights_cache):
+    wl, steps = SMALL[name]
+    print(f"case {name} mode {mode} H={wl.H} V={wl.V} B={wl.B} k={wl.k} {wl.dtype}", flush=True)
+    W_store, W64, Wd = _weights(weights_cache, wl)
+    positions = excused = 0
+    for step in range(steps):
+        case = Case(wl, W_store, W64, step, Wd)
+        res = gpu_run(case, mode)
+        ora = oracle_run(case, mode)
+        assert res["err"] == 0
+        check_invariants(res, case.drafts, wl.k)
+        check_numerics(res, ora, mode, wl)
+        n, e, fails = compare_outcomes(mode, res, ora, wl.k)
+        assert not fails, fails
+        positions += n
+        excused += e
+    assert excused <= EXCUSE_RATE * positions + (1 if positions < 1000 else 0), (excused, positions)
+
+
+def test_out_of_range_drafts_are_rejected(weights_cache):
+    wl = C(H=128, V=700, B=4, k=3, cid=110)
+    W_store, W64, Wd = _weights(weights_cache, wl)
+    case = Case(wl, W_store, W64, 0, Wd)
+    bad = case.drafts.copy()
+    bad[0, 0] = -1
+    bad[1, 1] = wl.V
+    bad[2, 2] = wl.V + 1000
+    bad_d = torch.from_numpy(bad).to(dev())
+    for mode in ("greedy", "sample"):
+        res = gpu_run(case, mode, drafts_d=bad_d)
+        ora = oracle_run(case, mode, drafts=bad)
+        assert res["err"] == mv.DEVERR_DRAFT_RANGE
+        assert res["a"][0] == 0 and res["a"][1] <= 1 and res["a"][2] <= 2
+        n, e, fails = compare_outcomes(mode, res, ora, wl.k)
+        assert not fails and e == 0
+    # a clean call clears the error word
+    assert gpu_run(case, "greedy")["err"] == 0
+
+
+def test_drafts_equal_to_target_argmax_keep_everything(weights_cache):
+    wl = C(H=256, V=1500, B=6, k=4, cid=111)
+    W_store, W64, Wd = _weights(weights_cache, wl)
+    case = Case(wl, W_store, W64, 0, Wd)
+    L = oracle.lm_head_logits(case.Xt, W64)
+    g = np.argmax(L, axis=-1).astype(np.int32)
+    d = torch.from_numpy(np.ascontiguousarray(g[:, : wl.k])).to(dev())
+    res = gpu_run(case, "greedy", drafts_d=d)
+    assert np.all(res["a"] == wl.k)
+    assert np.array_equal(res["out"], g)
+
+
+def test_drafter_rows_equal_to_target_rows_keep_everything(weights_cache):
+    wl = C(H=256, V=1500, B=6, k=4, T=0.9, cid=112)
+    W_store, W64, Wd = _weights(weights_cache, wl)
+    case = Case(wl, W_store, W64, 0, Wd)
+    same = case.xt_d[:, : wl.k].contiguous()
+    res = gpu_run(case, "sample", xd_d=same)
+    assert np.all(res["a"] == wl.k)
+    ora = oracle_run(case, "sample", Xd=case.Xt[:, : wl.k])
+    assert np.all(ora["a"] == wl.k)
+    n, e, fails = compare_outcomes("sample", res, ora, wl.k)
+    assert not fails
+
+
+def test_bit_reproducible(weights_cache):
+    wl = C(H=512, V=5000, B=3, k=3, T=0.8, cid=101)
+    W_store, W64, Wd = _weights(weights_cache, wl)
+    case = Case(wl, W_store, W64, 1, Wd)
+    for mode in ("greedy", "sample"):
+        r1, r2 = gpu_run(case, mode), gpu_run(case, mode)
+        for key in ("a", "out", "logits", "probs", "row_stats", "pd_qd"):
+            assert np.array_equal(r1[key], r2[key]), (mode, key)
+
+
+@pytest.mark.parametrize("wl", [C(H=256, V=3000, B=5, k=3, T=0.8, cid=113),
+                                C(H=64, V=300, B=3, k=2, dtype="f32", cid=114)])
+def test_drafter_call_matches_oracle(wl, weights_cache):
+    W_store, W64, Wd = _weights(weights_cache, wl)
+    code = mv.DTYPE_BF16 if wl.dtype == "bf16" else mv.DTYPE_F32
+    ws = mv.alloc_workspace(mv.MODE_DRAFT, wl.B, wl.k, wl.H, wl.V, code, dev())
+    total = excused = 0
+    for step in range(10):
+        case = Case(wl, W_store, W64, step, Wd)
+        out = torch.full((wl.B, wl.k), -7, dtype=torch.int32, device=dev())
+        mv.spec_draft_sample(case.xd_d, Wd, wl.T, wl.seed, step, 0, out, ws)
+        got = out.cpu().numpy()
+        Q = oracle.softmax(oracle.lm_head_logits(case.Xd, W64), wl.T)
+        _, _, u_draft = oracle.verify_uniforms(wl.seed, step, wl.B, wl.k)
+        tok, lo, hi = oracle.inverse_cdf(Q.reshape(-1, wl.V), u_draft.reshape(-1))
+        assert np.array_equal(tok.reshape(wl.B, wl.k), case.drafts)
+        diff = got.reshape(-1) != tok
+        near = (np.abs(u_draft.reshape(-1) - lo) <= 1e-5) | (np.abs(u_draft.reshape(-1) - hi) <= 1e-5)
+        assert not np.any(diff & ~near)
+        excused += int(np.sum(diff))
+        total += diff.size
+    assert excused <= EXCUSE_RATE * total + 1
+    # depth offset: a chained drafter calls once per depth; row 0 of a call with
+    # depth0 = 1 draws with slot 1's uniform, i.e. reproduces the draft of slot 1
+    case = Case(wl, W_store, W64, 0, Wd)
+    one = case.xd_d[:, 1:2].contiguous()
+    out = torch.full((wl.B, 1), -7, dtype=torch.int32, device=dev())
+    mv.spec_draft_sample(one, Wd, wl.T, wl.seed, 0, 1,
+                         out, mv.alloc_workspace(mv.MODE_DRAFT, wl.B, 1, wl.H, wl.V, code, dev()))
+    Q = oracle.softmax(oracle.lm_head_logits(case.Xd[:, 1], W64), wl.T)
+    _, _, u_draft = oracle.verify_uniforms(wl.seed, 0, wl.B, wl.k)
+    tok, lo, hi = oracle.inverse_cdf(Q, u_draft[:, 1])
+    assert np.array_equal(tok, case.drafts[:, 1])
+    got = out.cpu().numpy()[:, 0]
+    near = (np.abs(u_draft[:, 1] - lo) <= 1e-5) | (np.abs(u_draft[:, 1] - hi) <= 1e-5)
+    assert not np.any((got != tok) & ~near)
