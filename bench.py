@@ -1,0 +1,238 @@
+"""Benchmark of the vocab-side verify step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--mode greedy|sample]
+
+One step = one verify call (the whole hot path: LM-head stream + fused softmax/argmax
+epilogue, cross-block combine, acceptance decisions and prefix scan, and in sample
+mode the fp64 correction/bonus draws) over one batch of synthetic inputs already
+resident in HBM. The default workload is single-stream decode: H=4096, V=151936,
+bf16 head, B=1 request, k=3 drafts, greedy verification. Inputs cycle through a pool
+of distinct seeded steps; drafts are drawn beforehand by the library's own drafter
+call (Philox word 2) from the drafter hidden states.
+
+Prints one JSON line: verified positions/s (value), accepted tokens/s, the LM-head
+kernel's achieved HBM bandwidth against the 8 TB/s peak (kernel time from HIP events
+recorded by the library on the call's stream), the hardware-counter traffic recorded
+under profiles/ when it was taken on the current kernel source, and the CPU oracle
+timed on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+LMHEAD_SRC = os.path.join(ROOT, "mtp_draft_verification_amd", "csrc", "lmhead.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def lmhead_source_hash():
+    with open(LMHEAD_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def recorded_traffic(wl, mode):
+    """HBM bytes per LM-head launch from the committed counter summary, if it was
+    measured on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"lmhead_{wl.name}_{mode}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m_hash and m_bytes) or m_hash.group(1) != lmhead_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def algorithmic(wl, mode):
+    """Bytes and flops one LM-head launch must move / do: every W element once, every
+    hidden row once, and 2*M*H*V flops. Positions M = B(k+1) (+ B k drafter rows)."""
+    es = 2 if wl.dtype == "bf16" else 4
+    M = wl.M_eff(mode)
+    bytes_ = wl.V * wl.H * es + M * wl.H * es
+    flops = 2.0 * M * wl.H * wl.V
+    return bytes_, flops
+
+
+def cpu_baseline(wl, mode, W_store, budget_s):
+    """The oracle as it stands, on this host's cores, over a bounded number of steps."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    decode = oracle.decode_bf16 if wl.dtype == "bf16" else (lambda a: np.asarray(a, dtype=np.float64))
+    W64 = decode(W_store)
+    n = 0
+    t_total = 0.0
+    accepted = 0
+    while n < 3 or (t_total < budget_s and n < wl.steps):
+        xt, xd = synth.hidden(wl, n)
+        Xt, Xd = decode(xt), decode(xd)
+        drafts, _ = oracle.draft_from_hidden(Xd, W64, wl.T, wl.seed, n)   # input preparation, untimed
+        t0 = time.perf_counter()
+        if mode == "greedy":
+            r = oracle.verify_greedy_from_hidden(Xt, W64, drafts)
+        else:
+            r = oracle.verify_sample_from_hidden(Xt, Xd, W64, drafts, wl.T, wl.seed, n)
+        t_total += time.perf_counter() - t0
+        accepted += int(r["a"].sum())
+        n += 1
+    pos = wl.B * (wl.k + 1) * n
+    return {"value": pos / t_total, "unit": "positions/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} steps of the same workload ({pos} verified positions), fp64 numpy, "
+                      f"{t_total:.1f} s of oracle time; accepted tokens/s {accepted / t_total:.3g}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--mode", choices=["greedy", "sample"], default=None)
+    ap.add_argument("--pool", type=int, default=32, help="distinct seeded input steps cycled through")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="also run the library's plain copy kernel on this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the verify step is data parallel "
+              "across requests, so N GPUs each run this same single-GPU workload on their own requests.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mtp_draft_verification_amd as mv
+
+    wl = synth.CONFIGS[args.config]
+    mode = args.mode or wl.modes[0]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    code = mv.DTYPE_BF16 if wl.dtype == "bf16" else mv.DTYPE_F32
+    B, k, H, V = wl.B, wl.k, wl.H, wl.V
+
+    def to_dev(a):
+        if wl.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    log(f"workload {wl.name} mode {mode}: generating W [{V}, {H}] {wl.dtype}")
+    t0 = time.time()
+    W_store = synth.weights(wl)
+    Wd = to_dev(W_store)
+    log(f"  W ready in {time.time() - t0:.1f} s")
+    P = max(1, min(args.pool, args.steps + args.warmup))
+    xt_pool, xd_pool, d_pool = [], [], []
+    ws_draft = mv.alloc_workspace(mv.MODE_DRAFT, B, k, H, V, code, dev) if k > 0 else None
+    for s in range(P):
+        xt, xd = synth.hidden(wl, s)
+        xt_pool.append(to_dev(xt))
+        xd_pool.append(to_dev(xd))
+        d = torch.zeros((B, k), dtype=torch.int32, device=dev)
+        if k > 0:
+            mv.spec_draft_sample(xd_pool[-1], Wd, wl.T, wl.seed, s, 0, d, ws_draft)
+        d_pool.append(d)
+    torch.cuda.synchronize()
+    del ws_draft
+
+    ws = mv.alloc_workspace(mv.MODE_GREEDY if mode == "greedy" else mv.MODE_SAMPLE, B, k, H, V, code, dev)
+    K = args.steps
+    alen = torch.zeros((K + args.warmup, B), dtype=torch.int32, device=dev)
+    outt = torch.zeros((K + args.warmup, B, k + 1), dtype=torch.int32, device=dev)
+
+    def step(i, slot):
+        s = i % P
+        if mode == "greedy":
+            mv.spec_verify_greedy(xt_pool[s], Wd, d_pool[s], alen[slot], outt[slot], ws)
+        else:
+            mv.spec_verify_sample(xt_pool[s], xd_pool[s], Wd, d_pool[s], wl.T, wl.seed, s, alen[slot],
+                                  outt[slot], ws)
+
+    for i in range(args.warmup):
+        step(i, K + i)
+    torch.cuda.synchronize()
+    mv.timing_enable(True)
+    mv.timing_read(reset=True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(K):
+        step(i, i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    kern_ms, nlaunch = mv.timing_read(reset=True)
+    mv.timing_enable(False)
+    assert nlaunch == K, (nlaunch, K)
+    if mv.device_error(ws) != 0:
+        raise RuntimeError("device error word set during the benchmark")
+
+    if args.calibrate_copy_mib > 0:
+        nbytes = args.calibrate_copy_mib << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(5):
+            mv.copy_bytes(dst, src, nbytes)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {nbytes} bytes read and written per launch, 5 launches")
+
+    a_host = alen[:K].cpu().numpy()
+    accepted = int(a_host.sum())
+    positions = B * (k + 1) * K
+    value = positions / elapsed
+    alg_bytes, alg_flops = algorithmic(wl, mode)
+    kern_s = kern_ms / 1e3 / nlaunch
+    achieved = alg_bytes / kern_s / 1e9
+    traffic = recorded_traffic(wl, mode)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None if traffic is None else round(traffic / kern_s / 1e9, 1),
+                "kernel_us": round(kern_s * 1e6, 2), "algorithmic_bytes_per_launch": alg_bytes,
+                "mfma_tflops": round(alg_flops / kern_s / 1e12, 2),
+                "mfma_frac": round(alg_flops / kern_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    line = {
+        "metric": "verified positions/s (accepted tokens/s alongside) at 1 GPU; % of HBM roofline",
+        "value": round(value, 1),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0, 0.02) bf16 head, N(0,1) hidden, drafts drawn from the drafter rows)",
+        "config": {"workload": f"{wl.name}_{mode}", "H": H, "V": V, "B": B, "k": k, "mode": mode, "T": wl.T,
+                   "positions_per_step": B * (k + 1), "head_rows_per_step": wl.M_eff(mode)},
+        "accepted_tokens_per_s": round(accepted / elapsed, 2),
+        "emitted_tokens_per_s": round((accepted + B * K) / elapsed, 1),
+        "mean_acceptance_length": round(1 + accepted / (B * K), 4),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        line["cpu_baseline"] = cpu_baseline(wl, mode, W_store, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

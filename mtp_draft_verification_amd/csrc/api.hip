@@ -5,6 +5,7 @@
 #include "mtpv_internal.h"
 
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <utility>
@@ -16,9 +17,21 @@ namespace {
 
 constexpr int kMaxK = 64;
 constexpr int kLdsBudget = 64 * 1024;   // staging budget per workgroup (two workgroups fit per CU)
+constexpr size_t kLdsPerCU = 160 * 1024; // LDS of one gfx950 compute unit
+constexpr int kCUs = 256;                // compute units of one MI355X
 constexpr double kLog2e = 1.442695040888963407359924681001892137;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Per-wave K rotation in the few-position kernel (MTPV_SKINNY_ROTATE=0 turns it off).
+int skinny_rotate() {
+    static const int r = [] {
+        const char* e = std::getenv("MTPV_SKINNY_ROTATE");
+        return (e && std::atoi(e) == 0) ? 0 : 1;
+    }();
+    return r;
+}
+
 
 int shape_status(int mode, int B, int k, int H, int V, int dtype) {
     if (dtype != MTPV_BF16 && dtype != MTPV_F32) return MTPV_EDTYPE;
@@ -56,29 +69,54 @@ int make_plan(int mode, int B, int k, int H, int V, int dtype, Plan* pl) {
         p.Mt = B * (k + 1);
         p.Meff = p.Mt + (mode == MTPV_MODE_SAMPLE ? B * k : 0);
     }
-    // LM-head tile: positions in chunks of 16*nt, 16*va vocab rows per wave.
-    const int need = (p.Meff + 15) / 16;
-    if (p.es == 2) {
-        p.nt = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
-        p.va = p.nt == 1 ? 1 : 2;
-    } else {
-        p.va = 1;
-        p.nt = need <= 1 ? 1 : 2;
-    }
-    p.vblock = 64 * p.va;
-    p.S = (V + p.vblock - 1) / p.vblock;
-    p.MC = (p.Meff + 16 * p.nt - 1) / (16 * p.nt);
     const int epv = 16 / p.es;
-    const int kstep = 4 * epv;
-    const int rows = std::min(16 * p.nt, p.Meff);
-    const int h_pad = (H + kstep - 1) / kstep * kstep;
-    int kc = ((kLdsBudget / rows - 16) / p.es) / kstep * kstep;
-    if (kc < kstep) kc = kstep;
-    p.kc = std::min(kc, h_pad);
-    const size_t stage = (size_t)rows * (p.kc * p.es + 16);
-    const size_t red = (size_t)4 * 16 * p.nt * sizeof(Partial);
-    p.lds = std::max(stage, red);
-    p.grid = p.MC == 1 ? p.S : ((p.S + 7) / 8) * 8 * p.MC;
+    // Few positions (<= 16) whose hidden states fit in LDS: the streaming kernel
+    // with 4-row tiles (p.tiles tiles per wave, 16 * tiles rows per workgroup).
+    {
+        const int ks = 16 * epv;
+        const int nsteps = (H + ks - 1) / ks;
+        const size_t pitch = (size_t)nsteps * ks * p.es + 64;
+        const size_t x_lds = (size_t)p.Meff * pitch;
+        if (p.Meff <= 16 && x_lds <= (size_t)kLdsBudget) {
+            // One resident round: kCUs compute units times the workgroups their LDS
+            // holds, but no more workgroups than there are 16-row groups of tiles.
+            p.skinny = 1;
+            const int per_cu = (int)std::min<size_t>(8, kLdsPerCU / std::max<size_t>(x_lds, 1024));
+            const int tiles = (V + 3) / 4;
+            p.grid = std::max(1, std::min(kCUs * std::max(per_cu, 1), (tiles + 3) / 4));
+            p.tiles = (tiles + 4 * p.grid - 1) / (4 * p.grid);
+            p.vblock = 0;
+            p.S = p.grid;
+            p.MC = 1;
+            p.lds = std::max(x_lds, (size_t)4 * 16 * 16);
+            p.va = p.nt = 0;
+            p.kc = H;
+        }
+    }
+    if (!p.skinny) {
+        // LM-head tile: positions in chunks of 16*nt, 16*va vocab rows per wave.
+        const int need = (p.Meff + 15) / 16;
+        if (p.es == 2) {
+            p.nt = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
+            p.va = p.nt == 1 ? 1 : 2;
+        } else {
+            p.va = 1;
+            p.nt = need <= 1 ? 1 : 2;
+        }
+        p.vblock = 64 * p.va;
+        p.S = (V + p.vblock - 1) / p.vblock;
+        p.MC = (p.Meff + 16 * p.nt - 1) / (16 * p.nt);
+        const int kstep = 4 * epv;
+        const int rows = std::min(16 * p.nt, p.Meff);
+        const int h_pad = (H + kstep - 1) / kstep * kstep;
+        int kc = ((kLdsBudget / rows - 16) / p.es) / kstep * kstep;
+        if (kc < kstep) kc = kstep;
+        p.kc = std::min(kc, h_pad);
+        const size_t stage = (size_t)rows * (p.kc * p.es + 16);
+        const size_t red = (size_t)4 * 16 * p.nt * sizeof(Partial);
+        p.lds = std::max(stage, red);
+        p.grid = p.MC == 1 ? p.S : ((p.S + 7) / 8) * 8 * p.MC;
+    }
     // sampling jobs
     p.ntiles = (V + 63) / 64;
     p.NJ = mode == MTPV_MODE_GREEDY ? 0 : mode == MTPV_MODE_SAMPLE ? B : B * k;
@@ -210,10 +248,13 @@ int run(const Plan& plan, const void* xt, const void* xd, const void* w, const i
     la.dlogit = dlogit;
     la.spill = spill;
     la.err = err;
+    la.tiles = plan.tiles;
+    la.rotate = skinny_rotate();
 
     std::pair<hipEvent_t, hipEvent_t>* ev = timing_slot();
     if (ev && hipEventRecord(ev->first, stream) != hipSuccess) return MTPV_EDEVICE;
-    if (launch_lmhead(plan, la, stream) != hipSuccess) return MTPV_ELAUNCH;
+    const hipError_t le = plan.skinny ? launch_skinny(plan, la, stream) : launch_lmhead(plan, la, stream);
+    if (le != hipSuccess) return MTPV_ELAUNCH;
     if (ev && hipEventRecord(ev->second, stream) != hipSuccess) return MTPV_EDEVICE;
 
     DecideArgs da;

@@ -72,6 +72,12 @@ __device__ __forceinline__ Partial merge_partial(Partial a, Partial b) {
     return o;
 }
 
+// W is read exactly once per call: non-temporal loads keep it from displacing
+// the staged positions and partials in the caches.
+__device__ __forceinline__ u32x4_t load_w(const uint8_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+
 template <int ES, int VA, int NT, int PF>
 __global__ __launch_bounds__(256) void lmhead_kernel(LmHeadArgs p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -150,69 +156,62 @@ __global__ __launch_bounds__(256) void lmhead_kernel(LmHeadArgs p) {
         }
     };
 
-    // Stream W over steps [g0, g1) against the staged chunk that starts at g0.
+    // W ring: wb[i] holds the fragments of the step currently PF - i steps ahead.
     // The loads are unconditional (clamped addresses) so the compiler can keep
     // PF steps of loads in flight and wait for exactly the one it needs.
-    auto stream = [&](int g0, int g1) {
-        u32x4_t wb[PF][VA];
+    u32x4_t wb[PF][VA];
+    auto prologue = [&](int g0, int g1) {
 #pragma unroll
         for (int i = 0; i < PF; ++i)
 #pragma unroll
-            for (int va = 0; va < VA; ++va)
-                wb[i][va] = *(const u32x4_t*)(wp[va] + w_off(min(g0 + i, g1 - 1)));
+            for (int va = 0; va < VA; ++va) wb[i][va] = load_w(wp[va] + w_off(min(g0 + i, g1 - 1)));
+    };
+    auto consume = [&](int i, int sl) {
+        u32x4_t xb[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int r = nt * 16 + lrow;
+            xb[nt] = (r < mrows) ? *(const u32x4_t*)(smem + r * ldsstride + (sl * KSTEP + lgrp * EPV) * ES) : zero4;
+        }
+#pragma unroll
+        for (int va = 0; va < VA; ++va)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) acc[va][nt] = Mma<ES>::run(wb[i][va], xb[nt], acc[va][nt]);
+    };
+    // Stream W over steps [g0, g1) against the staged chunk that starts at g0;
+    // the ring must already hold steps g0 .. g0 + PF - 1.
+    auto body = [&](int g0, int g1) {
         int g = g0;
         for (; g + PF <= g1; g += PF) {
 #pragma unroll
             for (int i = 0; i < PF; ++i) {
-                const int sl = g + i - g0;
-                u32x4_t xb[NT];
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const int r = nt * 16 + lrow;
-                    xb[nt] = (r < mrows) ? *(const u32x4_t*)(smem + r * ldsstride + (sl * KSTEP + lgrp * EPV) * ES)
-                                         : zero4;
-                }
-#pragma unroll
-                for (int va = 0; va < VA; ++va)
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) acc[va][nt] = Mma<ES>::run(wb[i][va], xb[nt], acc[va][nt]);
+                consume(i, g + i - g0);
                 const int gn = min(g + i + PF, g1 - 1);
 #pragma unroll
-                for (int va = 0; va < VA; ++va) wb[i][va] = *(const u32x4_t*)(wp[va] + w_off(gn));
+                for (int va = 0; va < VA; ++va) wb[i][va] = load_w(wp[va] + w_off(gn));
             }
         }
         // tail: fewer than PF steps left, their W already in registers
 #pragma unroll
-        for (int i = 0; i < PF; ++i) {
-            if (g + i < g1) {
-                const int sl = g + i - g0;
-                u32x4_t xb[NT];
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const int r = nt * 16 + lrow;
-                    xb[nt] = (r < mrows) ? *(const u32x4_t*)(smem + r * ldsstride + (sl * KSTEP + lgrp * EPV) * ES)
-                                         : zero4;
-                }
-#pragma unroll
-                for (int va = 0; va < VA; ++va)
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) acc[va][nt] = Mma<ES>::run(wb[i][va], xb[nt], acc[va][nt]);
-            }
-        }
+        for (int i = 0; i < PF; ++i)
+            if (g + i < g1) consume(i, g + i - g0);
     };
 
     if (nsteps <= steps_per_chunk) {
-        // All of H fits: stage once, then one uninterrupted stream over W.
+        // All of H fits: start the W stream, stage the positions once, then one
+        // uninterrupted stream over W.
+        prologue(0, nsteps);
         stage(0, nsteps);
         __syncthreads();
-        stream(0, nsteps);
+        body(0, nsteps);
     } else {
         for (int g0 = 0; g0 < nsteps; g0 += steps_per_chunk) {
             const int g1 = min(nsteps, g0 + steps_per_chunk);
             __syncthreads();
+            prologue(g0, g1);
             stage(g0, g1);
             __syncthreads();
-            stream(g0, g1);
+            body(g0, g1);
         }
     }
 

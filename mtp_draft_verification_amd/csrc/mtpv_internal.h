@@ -48,6 +48,8 @@ struct Plan {
     int S;           // vocab blocks
     int MC;          // M chunks
     int kc;          // hidden elements staged per LDS pass
+    int skinny;      // 1: few-position streaming kernel (4-row tiles), 0: 16x16 tile kernel
+    int tiles;       // skinny kernel: 4-row tiles per wave
     size_t lds;      // dynamic LDS bytes of the LM-head kernel
     int grid;        // LM-head workgroups (1-D, XCD-aware ordering when MC > 1)
     int NJ;          // inverse-CDF jobs (0 in greedy mode)
@@ -73,9 +75,12 @@ struct LmHeadArgs {
     float* dlogit;          // [Meff]
     float* spill;           // [Meff, V] or NULL
     int32_t* err;           // cleared by the first workgroup
+    int tiles;              // skinny kernel: 4-row tiles per wave
+    int rotate;             // skinny kernel: per-wave rotation of the K order
 };
 
 hipError_t launch_lmhead(const Plan& plan, const LmHeadArgs& args, hipStream_t stream);
+hipError_t launch_skinny(const Plan& plan, const LmHeadArgs& args, hipStream_t stream);
 
 struct DecideArgs {
     const Partial* partials;

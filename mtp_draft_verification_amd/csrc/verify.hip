@@ -68,8 +68,8 @@ __device__ __forceinline__ double slot_uniform(uint64_t seed, uint64_t offset, i
 
 // ------------------------------------------------------------ row combination
 struct Acc {
-    double x;
-    double z;
+    double x;   // running max (log2 units)
+    double z;   // sum of exp2(. - x)
     float bv;
     int bi;
 };
@@ -96,46 +96,86 @@ __device__ __forceinline__ Acc acc_shfl_xor(Acc a, int off) {
     return o;
 }
 
-// Block-wide fixed-order combine of row r's S partials; the result is valid in thread 0.
-__device__ Acc combine_row(const Partial* partials, int S, int r, Acc* sh) {
-    const int tid = threadIdx.x;
-    Acc a{-__builtin_inf(), 0.0, -__builtin_inff(), INT_MAX};
-    const Partial* row = partials + (size_t)r * S;
-    for (int s = tid; s < S; s += 256) {
-        const Partial q = row[s];
-        a = acc_merge(a, Acc{(double)q.x, (double)q.s, q.bv, q.bi});
-    }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) a = acc_merge(a, acc_shfl_xor(a, off));
-    if ((tid & 63) == 0) sh[tid >> 6] = a;
-    __syncthreads();
-    Acc o = sh[0];
-    if (tid == 0) {
-        for (int w = 1; w < 4; ++w) o = acc_merge(o, sh[w]);
-    }
-    __syncthreads();
-    return o;
+__device__ __forceinline__ int request_row(const DecideArgs& p, int b, int i) {
+    if (p.mode == 2) return b * p.k + i;
+    if (i <= p.k) return b * (p.k + 1) + i;
+    return p.Mt + b * p.k + (i - p.k - 1);
 }
 
+// One workgroup per request. Wave w merges rows w, w + 4, ... of the request:
+// each lane loads its share of the row's S partials (all loads of a batch issued
+// before any use), reduces them (max first, then one exp2 per partial, no serial
+// exp chain), and a wave butterfly finishes the row; all in a fixed order. While
+// the waves reduce, the decision inputs (draft ids, draft logits, Philox uniforms)
+// are fetched by other lanes. Then one slot per thread is decided and thread 0
+// scans for the first rejection. Draft mode only writes one sampling job per row.
 __global__ __launch_bounds__(256) void decide_kernel(DecideArgs p) {
-    __shared__ Acc sh[4];
+    constexpr int U = 16;
     __shared__ RowStat rows[129];
+    __shared__ int s_draft[64];
+    __shared__ float s_lt[64], s_ld[64];
+    __shared__ double s_u[64];
+    __shared__ int keep[64];
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int k = p.k;
-    // rows of this request, in the order: target 0..k (greedy / sample), drafter 0..k-1 (sample)
-    // draft mode: drafter rows 0..k-1 only
-    int nrows;
-    if (p.mode == 0) nrows = k + 1;
-    else if (p.mode == 1) nrows = 2 * k + 1;
-    else nrows = k;
-    for (int i = 0; i < nrows; ++i) {
-        int r;
-        if (p.mode == 2) r = b * k + i;
-        else if (i <= k) r = b * (k + 1) + i;
-        else r = p.Mt + b * k + (i - k - 1);
-        const Acc a = combine_row(p.partials, p.S, r, sh);
-        if (tid == 0) {
+    const int nrows = p.mode == 0 ? k + 1 : p.mode == 1 ? 2 * k + 1 : k;
+    const float ninf = -__builtin_inff();
+
+    // Decision inputs, independent of the row statistics. They are fetched by the
+    // last wave (after its rows' loads are issued) so no wave's partial loads wait
+    // behind them; the draft-logit loads do not depend on the draft ids (a logit
+    // slot of an out-of-range draft is never written and never used).
+    const int fetch_wave = min(3, max(0, nrows - 1) % 4);
+    auto fetch_inputs = [&]() {
+        if (p.mode != 2 && wave == fetch_wave && lane < k) {
+            const int j = lane;
+            const int d = p.drafts[b * k + j];
+            const float lt = p.dlogit[b * (k + 1) + j];
+            const float ld = p.mode == 1 ? p.dlogit[p.Mt + b * k + j] : 0.f;
+            s_draft[j] = d;
+            s_lt[j] = lt;
+            s_ld[j] = ld;
+            s_u[j] = p.mode == 1 ? slot_uniform(p.seed, p.offset, j, b, 0) : 0.0;
+        }
+    };
+    if (wave >= nrows) fetch_inputs();
+
+    for (int i = wave; i < nrows; i += 4) {
+        const int r = request_row(p, b, i);
+        const Partial* row = p.partials + (size_t)r * p.S;
+        Acc a{-__builtin_inf(), 0.0, ninf, INT_MAX};
+        for (int base = 0; base < p.S; base += 64 * U) {
+            Partial q[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int s = base + u * 64 + lane;
+                q[u] = s < p.S ? row[s] : Partial{ninf, 0.f, ninf, INT_MAX};
+            }
+            // this wave's last row: fetch the decision inputs while its loads are in flight
+            if (base == 0 && i + 4 >= nrows) fetch_inputs();
+            float m = ninf;
+#pragma unroll
+            for (int u = 0; u < U; ++u) m = fmaxf(m, q[u].x);
+            Acc t{(double)m, 0.0, ninf, INT_MAX};
+            if (m != ninf) {
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (q[u].x != ninf) t.z += (double)q[u].s * (double)exp2f(q[u].x - m);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (q[u].bv > t.bv || (q[u].bv == t.bv && q[u].bi < t.bi)) {
+                    t.bv = q[u].bv;
+                    t.bi = q[u].bi;
+                }
+            }
+            a = acc_merge(a, t);
+        }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) a = acc_merge(a, acc_shfl_xor(a, off));
+        if (lane == 0) {
             RowStat rs;
             rs.x = a.x;
             rs.z = a.z;
@@ -149,72 +189,72 @@ __global__ __launch_bounds__(256) void decide_kernel(DecideArgs p) {
                 p.dbg_rowstats[2 * r] = a.x * kLn2;
                 p.dbg_rowstats[2 * r + 1] = a.z;
             }
+            if (p.mode == 2) {  // drafter draw: one job per row, no decision
+                Job job;
+                job.row_p = r;
+                job.row_q = -1;
+                job.out_index = r;
+                job.pad = 0;
+                job.u = slot_uniform(p.seed, p.offset, p.depth0 + i, b, 2);
+                job.ref_p = a.x * kLn2;
+                job.ref_q = 0.0;
+                p.jobs[r] = job;
+            }
         }
     }
+    if (p.mode == 2) return;
     __syncthreads();
-    if (tid != 0) return;
 
-    if (p.mode == 2) {
-        for (int j = 0; j < k; ++j) {
-            const int r = b * k + j;
-            Job job;
-            job.row_p = r;
-            job.row_q = -1;
-            job.out_index = r;
-            job.pad = 0;
-            job.u = slot_uniform(p.seed, p.offset, p.depth0 + j, b, 2);
-            job.ref_p = rows[j].x * kLn2;
-            job.ref_q = 0.0;
-            p.jobs[r] = job;
-        }
-        return;
-    }
-
-    int a = k;
-    for (int j = 0; j < k; ++j) {
-        const int d = p.drafts[b * k + j];
+    if (tid < k) {
+        const int j = tid;
+        const int d = s_draft[j];
         const bool in_range = d >= 0 && d < p.V;
         if (!in_range) atomicOr(p.err, 1);
-        const int rt = b * (k + 1) + j;
         double pj = -1.0, qj = -1.0;
-        bool keep = false;
+        bool kp = false;
         if (in_range) {
             const RowStat& st = rows[j];
-            pj = exp2((double)(p.dlogit[rt] * p.c2f) - st.x) / st.z;
+            pj = exp2((double)(s_lt[j] * p.c2f) - st.x) / st.z;
             if (p.mode == 0) {
                 qj = 0.0;
-                keep = (d == st.bi);
+                kp = (d == st.bi);
             } else {
-                const int rd = p.Mt + b * k + j;
                 const RowStat& sd = rows[k + 1 + j];
-                qj = exp2((double)(p.dlogit[rd] * p.c2f) - sd.x) / sd.z;
-                const double u = slot_uniform(p.seed, p.offset, j, b, 0);
-                keep = u * qj < pj;
+                qj = exp2((double)(s_ld[j] * p.c2f) - sd.x) / sd.z;
+                kp = s_u[j] * qj < pj;
             }
         }
         if (p.dbg_pdqd) {
             p.dbg_pdqd[2 * (b * k + j)] = pj;
             p.dbg_pdqd[2 * (b * k + j) + 1] = qj;
         }
-        if (a == k && !keep) a = j;
+        keep[j] = kp ? 1 : 0;
     }
-    p.accepted_len[b] = a;
+    __syncthreads();
+    if (tid != 0) return;
+    int al = k;
+    for (int j = 0; j < k; ++j)
+        if (!keep[j]) {
+            al = j;
+            break;
+        }
+    p.accepted_len[b] = al;
     int32_t* out = p.out_tokens + (size_t)b * (k + 1);
     for (int j = 0; j <= k; ++j) {
         int t = -1;
-        if (j < a) t = p.drafts[b * k + j];
-        else if (j == a && p.mode == 0) t = rows[a].bi;
+        if (j < al) t = s_draft[j];
+        else if (j == al && p.mode == 0) t = rows[al].bi;
         out[j] = t;
     }
     if (p.mode == 1) {
         Job job;
-        job.row_p = b * (k + 1) + a;
-        job.row_q = (a < k) ? p.Mt + b * k + a : -1;
-        job.out_index = b * (k + 1) + a;
+        job.row_p = b * (k + 1) + al;
+        job.row_q = (al < k) ? p.Mt + b * k + al : -1;
+        job.out_index = b * (k + 1) + al;
         job.pad = 0;
-        job.u = slot_uniform(p.seed, p.offset, a, b, 1);
-        job.ref_p = rows[a].x * kLn2;
-        job.ref_q = (a < k) ? rows[k + 1 + a].x * kLn2 : 0.0;
+        job.u = slot_uniform(p.seed, p.offset, al, b, 1);
+        job.ref_p = rows[al].x * kLn2;
+        job.ref_q = (al < k) ? rows[k + 1 + al].x * kLn2 : 0.0;
         p.jobs[b] = job;
     }
 }
