@@ -33,16 +33,24 @@ import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-LMHEAD_SRC = os.path.join(ROOT, "mtp_draft_verification_amd", "csrc", "lmhead.hip")
+CSRC = os.path.join(ROOT, "mtp_draft_verification_amd", "csrc")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+LMHEAD_SOURCES = ("lmhead.hip", "skinny.hip", "mtpv_internal.h", "api.hip")
+
+
 def lmhead_source_hash():
-    with open(LMHEAD_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the sources that define the LM-head kernels and their launch plan."""
+    h = hashlib.sha256()
+    for f in LMHEAD_SOURCES:
+        h.update(f.encode())
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def recorded_traffic(wl, mode):

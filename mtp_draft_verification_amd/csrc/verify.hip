@@ -74,28 +74,6 @@ struct Acc {
     int bi;
 };
 
-__device__ __forceinline__ Acc acc_merge(Acc a, Acc b) {
-    const double ninf = -__builtin_inf();
-    Acc o;
-    o.x = fmax(a.x, b.x);
-    const double za = (a.x == ninf) ? 0.0 : a.z * exp2(a.x - o.x);
-    const double zb = (b.x == ninf) ? 0.0 : b.z * exp2(b.x - o.x);
-    o.z = za + zb;
-    const bool take_b = (b.bv > a.bv) || (b.bv == a.bv && b.bi < a.bi);
-    o.bv = take_b ? b.bv : a.bv;
-    o.bi = take_b ? b.bi : a.bi;
-    return o;
-}
-
-__device__ __forceinline__ Acc acc_shfl_xor(Acc a, int off) {
-    Acc o;
-    o.x = __shfl_xor(a.x, off);
-    o.z = __shfl_xor(a.z, off);
-    o.bv = __shfl_xor(a.bv, off);
-    o.bi = __shfl_xor(a.bi, off);
-    return o;
-}
-
 __device__ __forceinline__ int request_row(const DecideArgs& p, int b, int i) {
     if (p.mode == 2) return b * p.k + i;
     if (i <= p.k) return b * (p.k + 1) + i;
@@ -145,36 +123,58 @@ __global__ __launch_bounds__(256) void decide_kernel(DecideArgs p) {
     for (int i = wave; i < nrows; i += 4) {
         const int r = request_row(p, b, i);
         const Partial* row = p.partials + (size_t)r * p.S;
-        Acc a{-__builtin_inf(), 0.0, ninf, INT_MAX};
+        // Pass 1 over the row (usually one batch held in registers): the row max.
+        // Pass 2: every lane rescales its partial sums to that max with one exp2
+        // each; then plain fp64 sums. No exp2 inside the cross-lane reduction.
+        float m = ninf;
+        double z = 0.0;
+        float bv = ninf;
+        int bi = INT_MAX;
+        const bool one_batch = p.S <= 64 * U;
+        Partial q[U];
         for (int base = 0; base < p.S; base += 64 * U) {
-            Partial q[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int s = base + u * 64 + lane;
                 q[u] = s < p.S ? row[s] : Partial{ninf, 0.f, ninf, INT_MAX};
             }
-            // this wave's last row: fetch the decision inputs while its loads are in flight
-            if (base == 0 && i + 4 >= nrows) fetch_inputs();
-            float m = ninf;
-#pragma unroll
-            for (int u = 0; u < U; ++u) m = fmaxf(m, q[u].x);
-            Acc t{(double)m, 0.0, ninf, INT_MAX};
-            if (m != ninf) {
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-                    if (q[u].x != ninf) t.z += (double)q[u].s * (double)exp2f(q[u].x - m);
-            }
+            if (base == 0 && i + 4 >= nrows) fetch_inputs();  // overlap with this wave's loads
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                if (q[u].bv > t.bv || (q[u].bv == t.bv && q[u].bi < t.bi)) {
-                    t.bv = q[u].bv;
-                    t.bi = q[u].bi;
+                m = fmaxf(m, q[u].x);
+                if (q[u].bv > bv || (q[u].bv == bv && q[u].bi < bi)) {
+                    bv = q[u].bv;
+                    bi = q[u].bi;
                 }
             }
-            a = acc_merge(a, t);
         }
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) a = acc_merge(a, acc_shfl_xor(a, off));
+        for (int off = 1; off < 64; off <<= 1) {
+            m = fmaxf(m, __shfl_xor(m, off));
+            const float obv = __shfl_xor(bv, off);
+            const int obi = __shfl_xor(bi, off);
+            if (obv > bv || (obv == bv && obi < bi)) {
+                bv = obv;
+                bi = obi;
+            }
+        }
+        if (m != ninf) {
+            for (int base = 0; base < p.S; base += 64 * U) {
+                if (!one_batch) {
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int s = base + u * 64 + lane;
+                        q[u] = s < p.S ? row[s] : Partial{ninf, 0.f, ninf, INT_MAX};
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (q[u].x != ninf) z += (double)q[u].s * (double)exp2f(q[u].x - m);
+            }
+        }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) z += __shfl_xor(z, off);
+        const Acc a{(double)m, z, bv, bi};
         if (lane == 0) {
             RowStat rs;
             rs.x = a.x;

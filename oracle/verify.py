@@ -43,7 +43,9 @@ def lm_head_logits(X, W):
     """
     X = np.asarray(X, dtype=np.float64)
     W = np.asarray(W, dtype=np.float64)
-    return X @ W.T
+    lead = X.shape[:-1]
+    # one matrix product over all rows (a stacked product would re-read W per row block)
+    return (X.reshape(-1, X.shape[-1]) @ W.T).reshape(lead + (W.shape[0],))
 
 
 def softmax(L, T=1.0):
