@@ -1,6 +1,6 @@
 """Benchmark of the vocab-side verify step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--mode greedy|sample]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--mode greedy|sample]
 
 One step = one verify call (the whole hot path: LM-head stream + fused softmax/argmax
 epilogue, cross-block combine, acceptance decisions and prefix scan, and in sample
@@ -113,7 +113,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=2,
+                    help="1 tiny fp32, 2 decode, 3 batched sampling, 4 depth-5 chain, 5 rollout")
     ap.add_argument("--mode", choices=["greedy", "sample"], default=None)
     ap.add_argument("--pool", type=int, default=32, help="distinct seeded input steps cycled through")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
@@ -131,7 +132,7 @@ def main():
     import torch
     import mtp_draft_verification_amd as mv
 
-    wl = synth.CONFIGS[args.config]
+    wl = synth.WORKLOADS[args.workload]
     mode = args.mode or wl.modes[0]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -61,7 +61,7 @@ def _decay_rho(base, k):
     return tuple(base ** d for d in range(1, k + 1))
 
 
-CONFIGS = {
+WORKLOADS = {
     1: Workload(1, "tiny_f32_H256_V4096_B4_k3", 256, 4096, 4, 3, "f32", 1.0 / math.sqrt(256),
                 _const_rho(0.8, 3), 1.0, ("greedy", "sample"), 1),
     2: Workload(2, "decode_H4096_V151936_B1_k3", 4096, 151936, 1, 3, "bf16", 0.02,

@@ -18,7 +18,7 @@ from gpu_util import TOL_LOGIT, TOL_PROB, WINDOW, compare_outcomes, decode, dev,
 
 pytestmark = pytest.mark.gpu
 
-# config id -> (modes, requests the oracle checks)
+# workload id -> (modes, requests the oracle checks)
 CASES = {2: (("greedy",), [0]), 3: (("sample",), [0, 5, 13, 31]), 4: (("greedy", "sample"), [0, 21, 42, 63]),
          5: (("sample",), [0, 77, 160, 255])}
 
@@ -31,7 +31,7 @@ def loaded():
 def _load(cache, cid):
     if cid not in cache:
         cache.clear()  # keep one head at a time in host memory
-        wl = synth.CONFIGS[cid]
+        wl = synth.WORKLOADS[cid]
         print(f"loading workload {wl.name}", flush=True)
         W_store = synth.weights(wl)
         W64 = decode(W_store, wl.dtype)

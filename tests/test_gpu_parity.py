@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 
 C = synth.custom
 SMALL = {
-    "cfg1_tiny_f32": (synth.CONFIGS[1], 60),
+    "tiny_f32": (synth.WORKLOADS[1], 60),
     "ragged_vocab_bf16": (C(H=512, V=5000, B=3, k=3, T=0.8, cid=101), 12),
     "ragged_hidden_bf16": (C(H=264, V=1000, B=2, k=2, cid=102), 12),
     "position_chunks_bf16": (C(H=256, V=3000, B=40, k=3, T=0.9, cid=103), 3),

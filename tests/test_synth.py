@@ -36,6 +36,6 @@ def test_hidden_correlation():
 
 
 def test_configs_shapes():
-    c = synth.CONFIGS
+    c = synth.WORKLOADS
     assert (c[2].M_t, c[3].M_eff("sample"), c[4].M_t, c[5].M_eff("sample")) == (4, 224, 384, 1792)
     assert c[1].dtype == "f32" and c[3].T == 0.7 and c[4].rho[0] == 0.9
