@@ -40,7 +40,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-LMHEAD_SOURCES = ("lmhead.hip", "skinny.hip", "mtpv_internal.h", "api.hip")
+LMHEAD_SOURCES = ("lmhead.hip", "skinny.hip", "wide.hip", "mtpv_internal.h", "api.hip")
 
 
 def lmhead_source_hash():

@@ -23,10 +23,11 @@ constexpr double kLog2e = 1.442695040888963407359924681001892137;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Per-wave K rotation in the few-position kernel (MTPV_SKINNY_ROTATE=0 turns it off).
-int skinny_rotate() {
+// Rotation of the K order per wave / workgroup in the streaming kernels
+// (MTPV_K_ROTATE=0 turns it off, for measurements).
+int k_rotate() {
     static const int r = [] {
-        const char* e = std::getenv("MTPV_SKINNY_ROTATE");
+        const char* e = std::getenv("MTPV_K_ROTATE");
         return (e && std::atoi(e) == 0) ? 0 : 1;
     }();
     return r;
@@ -80,7 +81,7 @@ int make_plan(int mode, int B, int k, int H, int V, int dtype, Plan* pl) {
         if (p.Meff <= 16 && x_lds <= (size_t)kLdsBudget) {
             // One resident round: kCUs compute units times the workgroups their LDS
             // holds, but no more workgroups than there are 16-row groups of tiles.
-            p.skinny = 1;
+            p.kind = KIND_SKINNY;
             const int per_cu = (int)std::min<size_t>(8, kLdsPerCU / std::max<size_t>(x_lds, 1024));
             const int tiles = (V + 3) / 4;
             p.grid = std::max(1, std::min(kCUs * std::max(per_cu, 1), (tiles + 3) / 4));
@@ -93,7 +94,23 @@ int make_plan(int mode, int B, int k, int H, int V, int dtype, Plan* pl) {
             p.kc = H;
         }
     }
-    if (!p.skinny) {
+    if (p.kind != KIND_SKINNY && p.es == 2) {
+        // Many positions, bf16: one workgroup per CU over 1/256 of the vocabulary
+        // (fewer ranges for small V, at least 64 rows each), positions in chunks of
+        // at most 128 (32 * nt: two halves of 16 * nt; more accumulators would
+        // spill), the chunks of one range on one XCD.
+        p.kind = KIND_WIDE;
+        p.MC = (p.Meff + 127) / 128;
+        const int per = (p.Meff + p.MC - 1) / p.MC;
+        p.nt = (per + 31) / 32;  // position fragments per wave (two halves per chunk)
+        p.va = 4;
+        p.S = std::max(1, std::min(kCUs, (V + 63) / 64));
+        p.grid = p.MC == 1 ? p.S : ((p.S + 7) / 8) * 8 * p.MC;
+        p.lds = wide_lds_bytes(p.nt);
+        p.kc = 128;
+        p.vblock = 0;
+    }
+    if (p.kind == KIND_TILE) {
         // LM-head tile: positions in chunks of 16*nt, 16*va vocab rows per wave.
         const int need = (p.Meff + 15) / 16;
         if (p.es == 2) {
@@ -249,11 +266,13 @@ int run(const Plan& plan, const void* xt, const void* xd, const void* w, const i
     la.spill = spill;
     la.err = err;
     la.tiles = plan.tiles;
-    la.rotate = skinny_rotate();
+    la.rotate = k_rotate();
 
     std::pair<hipEvent_t, hipEvent_t>* ev = timing_slot();
     if (ev && hipEventRecord(ev->first, stream) != hipSuccess) return MTPV_EDEVICE;
-    const hipError_t le = plan.skinny ? launch_skinny(plan, la, stream) : launch_lmhead(plan, la, stream);
+    const hipError_t le = plan.kind == KIND_SKINNY ? launch_skinny(plan, la, stream)
+                          : plan.kind == KIND_WIDE ? launch_wide(plan, la, stream)
+                                                   : launch_lmhead(plan, la, stream);
     if (le != hipSuccess) return MTPV_ELAUNCH;
     if (ev && hipEventRecord(ev->second, stream) != hipSuccess) return MTPV_EDEVICE;
 

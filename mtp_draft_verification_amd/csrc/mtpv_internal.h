@@ -39,16 +39,19 @@ struct Job {
     double ref_q;
 };
 
+enum { KIND_TILE = 0, KIND_SKINNY = 1, KIND_WIDE = 2 };
+
 struct Plan {
     int mode, B, k, H, V, dtype;
     int es;          // element size (2 for bf16, 4 for fp32)
     int Mt, Meff;    // target rows, all rows the head sees
-    int va, nt;      // LM-head kernel tile: 16*va vocab rows per wave, 16*nt rows per M chunk
+    int va, nt;      // tile kernel: 16*va vocab rows per wave, 16*nt positions per chunk;
+                     // wide kernel: nt = position fragments (16*nt positions per chunk)
     int vblock;      // vocab rows per workgroup (64 * va)
     int S;           // vocab blocks
     int MC;          // M chunks
     int kc;          // hidden elements staged per LDS pass
-    int skinny;      // 1: few-position streaming kernel (4-row tiles), 0: 16x16 tile kernel
+    int kind;        // LM-head kernel: KIND_SKINNY, KIND_WIDE or KIND_TILE
     int tiles;       // skinny kernel: 4-row tiles per wave
     size_t lds;      // dynamic LDS bytes of the LM-head kernel
     int grid;        // LM-head workgroups (1-D, XCD-aware ordering when MC > 1)
@@ -76,11 +79,13 @@ struct LmHeadArgs {
     float* spill;           // [Meff, V] or NULL
     int32_t* err;           // cleared by the first workgroup
     int tiles;              // skinny kernel: 4-row tiles per wave
-    int rotate;             // skinny kernel: per-wave rotation of the K order
+    int rotate;             // skinny / wide kernels: rotation of the K order per wave / workgroup
 };
 
 hipError_t launch_lmhead(const Plan& plan, const LmHeadArgs& args, hipStream_t stream);
 hipError_t launch_skinny(const Plan& plan, const LmHeadArgs& args, hipStream_t stream);
+hipError_t launch_wide(const Plan& plan, const LmHeadArgs& args, hipStream_t stream);
+size_t wide_lds_bytes(int fm);
 
 struct DecideArgs {
     const Partial* partials;

@@ -213,40 +213,43 @@ __global__ __launch_bounds__(256) void skinny_kernel(LmHeadArgs p) {
             }
             acc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             const int m = 4 * g + li;
-            if (m >= mrows) continue;
             float tx = ninf;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 if (v0 + e < V) tx = fmaxf(tx, a[e] * c2);
-            if (tx == ninf) continue;  // tile entirely past V
-            Stat s = st[g];
-            const float nx = fmaxf(s.x, tx);
-            float sum = (s.x == ninf) ? 0.f : s.s * exp2f(s.x - nx);
+            if (m < mrows && tx != ninf) {  // else: no position here, or tile past V
+                Stat s = st[g];
+                const float nx = fmaxf(s.x, tx);
+                float sum = (s.x == ninf) ? 0.f : s.s * exp2f(s.x - nx);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int v = v0 + e;
-                if (v < V) {
-                    sum += exp2f(a[e] * c2 - nx);
-                    if (a[e] > s.bv) {
-                        s.bv = a[e];
-                        s.bi = v;
+                for (int e = 0; e < 4; ++e) {
+                    const int v = v0 + e;
+                    if (v < V) {
+                        sum += exp2f(a[e] * c2 - nx);
+                        if (a[e] > s.bv) {
+                            s.bv = a[e];
+                            s.bi = v;
+                        }
                     }
                 }
-            }
-            s.x = nx;
-            s.s = sum;
-            st[g] = s;
-            if (lb == 0) {
-                const int d = dtok[g];
-                if (d >= v0 && d < v0 + 4) p.dlogit[m] = a[d - v0];
-                if (p.spill != nullptr) {
-                    float* dst = p.spill + (size_t)m * V + v0;
-                    if (vec_spill && v0 + 3 < V) {
-                        *(f32x4_t*)dst = a;
-                    } else {
+                s.x = nx;
+                s.s = sum;
+                st[g] = s;
+                if (lb == 0) {
+                    const int d = dtok[g];
+                    if (d >= v0 && d < v0 + 4) {
+                        const int t = d - v0;
+                        p.dlogit[m] = t == 0 ? a[0] : t == 1 ? a[1] : t == 2 ? a[2] : a[3];
+                    }
+                    if (p.spill != nullptr) {
+                        float* dst = p.spill + (size_t)m * V + v0;
+                        if (vec_spill && v0 + 3 < V) {
+                            *(f32x4_t*)dst = a;
+                        } else {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (v0 + e < V) dst[e] = a[e];
+                            for (int e = 0; e < 4; ++e)
+                                if (v0 + e < V) dst[e] = a[e];
+                        }
                     }
                 }
             }
