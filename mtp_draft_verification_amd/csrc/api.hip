@@ -95,19 +95,30 @@ int make_plan(int mode, int B, int k, int H, int V, int dtype, Plan* pl) {
         }
     }
     if (p.kind != KIND_SKINNY && p.es == 2) {
-        // Many positions, bf16: one workgroup per CU over 1/256 of the vocabulary
-        // (fewer ranges for small V, at least 64 rows each), positions in chunks of
-        // at most 128 (32 * nt: two halves of 16 * nt; more accumulators would
-        // spill), the chunks of one range on one XCD.
+        // Many positions, bf16: LDS-tiled matrix product, one workgroup per tile of at
+        // most 256 vocabulary rows by 128 or 256 positions (whichever pads fewer
+        // rows; 256 on a tie, so W is re-read from L2 fewer times), the position
+        // chunks of one vocabulary tile on one XCD. With few tiles the vocabulary is
+        // cut into more, smaller tiles so that every compute unit gets the same
+        // number (at least 16 rows per tile).
         p.kind = KIND_WIDE;
-        p.MC = (p.Meff + 127) / 128;
-        const int per = (p.Meff + p.MC - 1) / p.MC;
-        p.nt = (per + 31) / 32;  // position fragments per wave (two halves per chunk)
-        p.va = 4;
-        p.S = std::max(1, std::min(kCUs, (V + 63) / 64));
+        const int pad128 = (p.Meff + 127) / 128 * 128;
+        const int pad256 = (p.Meff + 255) / 256 * 256;
+        const int bm = pad256 <= pad128 ? 256 : 128;
+        p.nt = bm;
+        p.MC = (p.Meff + bm - 1) / bm;
+        p.va = 0;
+        const long long s0 = (V + wide_rows() - 1) / wide_rows();
+        long long S = s0;
+        if (s0 * p.MC < 4LL * kCUs) {
+            const long long rounds = (s0 * p.MC + kCUs - 1) / kCUs;
+            S = std::max(s0, (rounds * kCUs + p.MC - 1) / p.MC);
+            S = std::min(S, std::max(s0, (long long)(V + 15) / 16));
+        }
+        p.S = (int)S;
         p.grid = p.MC == 1 ? p.S : ((p.S + 7) / 8) * 8 * p.MC;
-        p.lds = wide_lds_bytes(p.nt);
-        p.kc = 128;
+        p.kc = 64;
+        p.lds = wide_lds_bytes(bm);
         p.vblock = 0;
     }
     if (p.kind == KIND_TILE) {

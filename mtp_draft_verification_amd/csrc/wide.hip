@@ -1,33 +1,31 @@
-// LM-head kernel for many positions (more than 16): batched verification and the
-// large-batch rollout shape.
+// LM-head kernel for many positions (more than 16, bf16): batched verification
+// and the large-batch rollout shape.
 //
 // The verify pass is a contraction l[m, v] = sum_h x[m, h] W[v, h] over every
-// target and drafter position m of the batch, with W read from HBM once ("One step
-// deeper than the main model" / "How the draft becomes real output", "The Tiny
-// Draft Model Hidden Inside Qwen": one shared head for target and drafter rows).
-// With hundreds of positions it approaches and then crosses the point where the
-// MFMA units, not HBM, set the pace ("Larger batches can also push the target model
-// from memory-bound toward compute-bound", same page).
+// target and drafter position m of the batch, with one head W for both ("The Tiny
+// Draft Model Hidden Inside Qwen", sections "One step deeper than the main model"
+// and "How the draft becomes real output"). With hundreds of positions it
+// approaches and then crosses the point where the MFMA units, not HBM, set the
+// pace (same page: larger batches push the target from memory-bound toward
+// compute-bound), so it is written as an LDS-tiled matrix product:
 //
-// Layout of the work:
-//  * one 8-wave workgroup per compute unit (two waves per SIMD), persistent over
-//    1/256 of the vocabulary (rows split evenly) and one chunk of at most 32*FM <=
-//    128 positions; with several position chunks, the chunks of one vocabulary
-//    range go to the same XCD side by side so that range's W is served from that
-//    XCD's L2 after the first read;
-//  * wave w owns column w % 4 of the range's rows and half w / 4 of the positions;
-//    the column is processed 64 rows (4 MFMA row fragments) at a time against the
-//    wave's 16*FM positions: 4*FM independent 16x16x32 bf16 MFMA accumulators;
-//  * W fragments go from HBM straight into registers with 16-byte loads, one K-chunk (4 steps of 32 hidden elements) ahead, the prefetch running
-//    on across chunk boundaries; the two waves of a column load the same W (the
-//    second from L2), every W byte comes from HBM once;
-//  * the positions' hidden states are staged through LDS in K-chunks of 128
-//    elements, double buffered (one barrier per K-chunk); B fragments are read with
-//    ds_read_b128: one 1 KB fragment feeds 4 MFMAs;
-//  * after each 64-row column chunk the wave folds its logits into running per-
-//    position statistics kept in LDS (max of l*c2, sum of exp2, argmax), gathers the
-//    draft logits and writes the fp32 logits out when asked; at the end the four
-//    columns are merged into one partial per (position, workgroup).
+//  * one workgroup (8 waves) per tile of BV = 256 vocabulary rows by BM positions
+//    (BM = 128 or 256); the tiles of one vocabulary block go to the same XCD side
+//    by side, so after the first one its W comes from that XCD's L2;
+//  * both operands are staged in LDS in K-stages of 64 hidden elements (128 bytes
+//    per row) with 16-byte direct-to-LDS loads: one load instruction fills 1 KB,
+//    eight whole 128-byte rows, so every cache line fetched is used in full and no
+//    register holds staged data; NS stages rotate (the loads of stage kb + NS - 1
+//    are issued while stage kb is multiplied);
+//  * within a staged row the eight 16-byte chunks are XOR-swizzled by row, which
+//    makes the MFMA fragment reads (ds_read_b128, 16 rows per 16 lanes) free of bank
+//    conflicts;
+//  * wave w owns vocabulary rows 64 (w % 4) .. + 63 and positions (w / 4) BM / 2 ..
+//    + BM / 2 - 1 of the tile: 4 x BM / 32 accumulators of 16x16x32 bf16 MFMAs;
+//  * after the last stage each wave folds its logits into per-position statistics
+//    (max of l * c2, sum of exp2, argmax), gathers the draft logits and writes the
+//    fp32 logits out when asked; the four vocabulary waves are merged into one
+//    partial per (position, vocabulary block).
 // Accumulation is fp32 over all of H in a fixed order; no split-K, no atomics.
 #include "mtpv_internal.h"
 
@@ -39,11 +37,15 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int KC = 128;                // hidden elements per staged K-chunk
-constexpr int KSTEP = 32;              // hidden elements per MFMA step
-constexpr int SPC = KC / KSTEP;        // MFMA steps per K-chunk
-constexpr int PITCH = KC * 2 + 16;     // LDS bytes per staged position row
+constexpr int BV = 256;        // vocabulary rows per tile
+constexpr int NT = 512;        // threads per workgroup
+constexpr int LDS_MAX = 160 * 1024;
+
+// Sixteen zero bytes: the source of the hidden-state chunks past H in the last
+// stage when H is not a multiple of 64 (a direct-to-LDS load cannot zero-fill).
+__device__ __attribute__((aligned(16))) const unsigned int kZero16[4] = {0u, 0u, 0u, 0u};
 
 struct WStat {
     float x, s, bv;
@@ -63,127 +65,168 @@ __device__ __forceinline__ WStat merge_wstat(WStat a, WStat b) {
     return o;
 }
 
-// W bytes are reused from L2: by the second wave of a column and by the other
-// position chunks of the range. Plain (temporal) loads, so the first read
-// allocates in L2.
-__device__ __forceinline__ u32x4_t load_w(const uint8_t* p) { return *reinterpret_cast<const u32x4_t*>(p); }
-
-// Position of the next W step to load: column chunk, K-chunk index (before
-// rotation), step within the K-chunk. A value type, advanced by a pure function,
-// so it stays in registers.
-struct WCursor {
-    int c, ki, s;
-};
-
-__device__ __forceinline__ WCursor advance(WCursor u, int nkc, int nch) {
-    // past the last step the cursor stays there (a re-read, no new traffic)
-    if (u.s + 1 < SPC) return WCursor{u.c, u.ki, u.s + 1};
-    if (u.ki + 1 < nkc) return WCursor{u.c, u.ki + 1, 0};
-    if (u.c + 1 < nch) return WCursor{u.c + 1, 0, 0};
-    return u;
+// s_waitcnt with only the vector-memory count set (expcnt and lgkmcnt at their
+// maxima): gfx9 encoding, vmcnt split over bits 3:0 and 15:14.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-struct WFrags {
-    u32x4_t f[4];
+// Tile of at most BV vocabulary rows by BM positions, K-stages of BK = 64 hidden
+// elements. W and the positions have rings of their own in LDS: NSW stages of W (the
+// operand that streams from HBM, so it runs one stage further ahead) and NSX of X.
+template <int BM>
+struct WideCfg {
+    static constexpr int BK = 64;
+    static constexpr int ROWB = BK * 2;                      // LDS bytes per staged row
+    static constexpr int CPR = BK / 8;                       // 16-byte chunks per staged row
+    static constexpr int RPI = 64 / CPR;                     // rows filled by one load instruction
+    static constexpr int WSTAGE = BV * ROWB;                 // bytes of one W stage
+    static constexpr int XSTAGE = BM * ROWB;                 // bytes of one X stage
+    static constexpr int NSX = BM == 256 ? 2 : 3;            // X stages
+    static constexpr int NSW = (LDS_MAX - NSX * XSTAGE) / WSTAGE;  // W stages
+    static constexpr int LPW_W = BV / RPI / (NT / 64);       // W load instructions per wave per stage
+    static constexpr int LPW_X = BM / RPI / (NT / 64);       // X load instructions per wave per stage
+    static constexpr int FM = BM / 32;                       // position fragments per wave
+    static constexpr int KS = BK / 32;                       // MFMA K-steps per stage
+    static constexpr int LDS = NSW * WSTAGE + NSX * XSTAGE;
+    static_assert(NSW >= NSX && NSX >= 2 && LDS <= LDS_MAX, "rings");
+    static_assert(LPW_W * RPI * (NT / 64) == BV && LPW_X * RPI * (NT / 64) == BM, "whole instructions");
+    // Loads issued after the later of X(kb) and W(kb), in issue order (each
+    // iteration i issues X(i + NSX - 1), then W(i + NSW - 1)).
+    static constexpr int WAIT = NSW > NSX ? LPW_W * (NSW - NSX) + (NSX - 2) * (LPW_W + LPW_X)
+                                          : (NSX - 2) * (LPW_W + LPW_X);
+    static_assert(NSW - NSX <= 1 && WAIT < 64, "wait count");
 };
 
-template <int FM>
+// Workgroup barrier for the stage ring. __syncthreads() would also make every wave
+// wait for all of its direct-to-LDS loads (vmcnt(0): its release fence covers them),
+// which drains the ring at every stage; the ring's own vmcnt wait already covers
+// the stage about to be read, so only the barrier itself is needed. The empty asm
+// statements keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void stage_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Chunk swizzle of staged row r: any 16 consecutive rows read at one chunk index
+// land on 16 distinct 16-byte bank groups (of a 256-byte bank row).
+template <int CPR>
+__device__ __forceinline__ int chunk_swz(int r) { return (r / (16 / CPR)) % CPR; }
+
+template <int BM>
 __global__ __launch_bounds__(512, 1) void wide_kernel(LmHeadArgs p) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    constexpr int NT = 512;        // threads per workgroup
-    constexpr int PF = SPC;        // W ring depth: one K-chunk, so a step's slot is its index
-    constexpr int ROWS = 32 * FM;  // position rows per chunk (two halves of 16 * FM)
-    uint8_t* xbuf0 = smem;
-    uint8_t* xbuf1 = smem + ROWS * PITCH;
-    WStat* stats = reinterpret_cast<WStat*>(smem + 2 * ROWS * PITCH);  // [4][ROWS]
-    int* dtok = reinterpret_cast<int*>(stats + 4 * ROWS);              // [ROWS] draft id per position
+    using Cfg = WideCfg<BM>;
+    constexpr int NSW = Cfg::NSW;
+    constexpr int NSX = Cfg::NSX;
+    constexpr int LPW_W = Cfg::LPW_W;
+    constexpr int LPW_X = Cfg::LPW_X;
+    constexpr int FM = Cfg::FM;
+    constexpr int BK = Cfg::BK;
+    constexpr int ROWB = Cfg::ROWB;
+    constexpr int CPR = Cfg::CPR;
+    constexpr int RPI = Cfg::RPI;
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    uint8_t* wring = smem;                            // NSW stages of BV rows
+    uint8_t* xring = smem + NSW * Cfg::WSTAGE;        // NSX stages of BM rows
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = (tid >> 6) & 3;  // vocabulary column
-    const int half = tid >> 8;        // half of the positions
-    const int lrow = lane & 15;
-    const int lgrp = lane >> 4;
+    const int wave = tid >> 6;
+    const int vw = wave & 3;   // vocabulary quarter of the tile
+    const int mw = wave >> 2;  // position half of the tile
     const int H = p.H;
     const int V = p.V;
-    const int R = p.S;  // vocabulary ranges (= partials per position)
+    const int S = p.S;  // vocabulary tiles (= partials per position)
 
-    // workgroup -> (range, position chunk); chunks of one range share an XCD
-    int rg, mc;
+    // workgroup -> (vocabulary tile, position chunk); the chunks of one tile share an XCD
+    int vt, mt;
     if (p.MC == 1) {
-        rg = blockIdx.x;
-        mc = 0;
+        vt = blockIdx.x;
+        mt = 0;
     } else {
-        const int L = blockIdx.x;
-        const int slot = L >> 3;
-        mc = slot % p.MC;
-        rg = (slot / p.MC) * 8 + (L & 7);
-        if (rg >= R) return;  // uniform over the workgroup
+        const int g = blockIdx.x;
+        const int idx = g >> 3;
+        mt = idx % p.MC;
+        vt = (idx / p.MC) * 8 + (g & 7);
+        if (vt >= S) return;  // uniform over the workgroup
     }
-    if (rg == 0 && mc == 0 && tid == 0) *p.err = 0;
+    if (vt == 0 && mt == 0 && tid == 0) *p.err = 0;
 
-    const int m0 = mc * ROWS;
-    const int mrows = min(ROWS, p.Meff - m0);
-    // this range's rows, and this wave's column of them
-    const int r0 = (int)((long long)rg * V / R);
-    const int r1 = (int)((long long)(rg + 1) * V / R);
-    const int n = r1 - r0;
-    const int cs = r0 + (int)((long long)wave * n / 4);
-    const int ce = r0 + (int)((long long)(wave + 1) * n / 4);
-    const int colmax = (n + 3) / 4;
-    const int nch = max(1, (colmax + 63) / 64);  // 64-row chunks, same count for all waves
-    const int nkc = (H + KC - 1) / KC;
-    const int total_it = nch * nkc;
+    // vocabulary rows [v0, v1) of this tile: the 16-row groups of V split evenly over
+    // the S tiles (edges on 16-row boundaries keep the fp32 spill's vector stores
+    // aligned; at most 16 groups per tile since S >= V / 256)
+    const int G = (V + 15) / 16;
+    const int v0 = min(V, 16 * (int)((long long)vt * G / S));
+    const int v1 = min(V, 16 * (int)((long long)(vt + 1) * G / S));
+    const int m0 = mt * BM;
+    const int nk = (H + BK - 1) / BK;
     const size_t rowbytes = (size_t)H * 2;
-    const int kc0 = p.rotate ? (int)(((unsigned)rg * 7u) % (unsigned)nkc) : 0;
+    // the position chunks of one vocabulary tile share its rotation (and its W in L2)
+    const int kb0 = p.rotate ? (int)(((unsigned)vt * 7u) % (unsigned)nk) : 0;
 
-    // ---------------------------------------------------------------- staging
-    const u32x4_t zero4 = u32x4_t{0u, 0u, 0u, 0u};
-    constexpr int VPR = KC * 2 / 16;               // 16-byte vectors per staged row
-    constexpr int NXV = (ROWS * VPR + NT - 1) / NT;  // vectors per thread
-    // Loads are unconditional (clamped addresses) so the compiler can count them
-    // exactly; rows past the chunk and elements past H are zeroed at store time.
-    u32x4_t xr[NXV];
-    int xk = 0;  // K-chunk of the values in xr
-    auto x_load = [&](int kc) {
-        xk = kc;
+    // ------------------------------------------------------------ stage loads
+    // W instruction j (j = wave * LPW_W + i) fills staged W rows RPI j .. RPI j + RPI - 1,
+    // X instruction j likewise for positions. Lane l writes LDS slot l % CPR of row
+    // RPI j + l / CPR and fetches chunk (l % CPR) ^ swz(row). Rows past the tile and
+    // positions past Meff re-read the last valid row (results ignored).
+    const uint8_t* w_row[LPW_W];
+    int w_chunk[LPW_W];
+    const uint8_t* x_row[LPW_X];
+    int x_chunk[LPW_X];
 #pragma unroll
-        for (int i = 0; i < NXV; ++i) {
-            const int e = tid + i * NT;
-            const int r = min(e / VPR, mrows - 1);
-            const int c = e % VPR;
-            const int kk = min(kc * KC + c * 8, H - 8);
-            const int gr = m0 + r;
-            const uint8_t* src = gr < p.Mt ? p.xt + (size_t)gr * rowbytes : p.xd + (size_t)(gr - p.Mt) * rowbytes;
-            xr[i] = *(const u32x4_t*)(src + (size_t)kk * 2);
+    for (int i = 0; i < LPW_W; ++i) {
+        const int r = RPI * (wave * LPW_W + i) + lane / CPR;
+        w_chunk[i] = (lane % CPR) ^ chunk_swz<CPR>(r);
+        w_row[i] = p.w + (size_t)min(v0 + r, v1 - 1) * rowbytes;
+    }
+#pragma unroll
+    for (int i = 0; i < LPW_X; ++i) {
+        const int r = RPI * (wave * LPW_X + i) + lane / CPR;
+        x_chunk[i] = (lane % CPR) ^ chunk_swz<CPR>(r);
+        const int m = min(m0 + r, p.Meff - 1);
+        x_row[i] = m < p.Mt ? p.xt + (size_t)m * rowbytes : p.xd + (size_t)(m - p.Mt) * rowbytes;
+    }
+    auto stage_k = [&](int kb) {
+        const int kk = kb + kb0;
+        return kk >= nk ? kk - nk : kk;
+    };
+    // chunks past H: W re-reads the row start, X reads sixteen zero bytes
+    auto issue_w = [&](int kb) {
+        const int kk = stage_k(kb);
+        uint8_t* dst = wring + (kb % NSW) * Cfg::WSTAGE + wave * LPW_W * 1024;
+#pragma unroll
+        for (int i = 0; i < LPW_W; ++i) {
+            const int k = kk * BK + 8 * w_chunk[i];
+            const uint8_t* src = k < H ? w_row[i] + (size_t)k * 2 : w_row[i];
+            __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + i * 1024), 16, 0, 0);
         }
     };
-    auto x_store = [&](uint8_t* buf) {
+    auto issue_x = [&](int kb) {
+        const int kk = stage_k(kb);
+        uint8_t* dst = xring + (kb % NSX) * Cfg::XSTAGE + wave * LPW_X * 1024;
 #pragma unroll
-        for (int i = 0; i < NXV; ++i) {
-            const int e = tid + i * NT;
-            const int r = e / VPR;
-            const int c = e - r * VPR;
-            const bool live = r < mrows && xk * KC + c * 8 < H;
-            if (r < ROWS) *(u32x4_t*)(buf + r * PITCH + c * 16) = live ? xr[i] : zero4;
+        for (int i = 0; i < LPW_X; ++i) {
+            const int k = kk * BK + 8 * x_chunk[i];
+            const uint8_t* src = k < H ? x_row[i] + (size_t)k * 2 : reinterpret_cast<const uint8_t*>(kZero16);
+            __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + i * 1024), 16, 0, 0);
         }
+    };
+    // iteration i issues X(i + NSX - 1), then W(i + NSW - 1), each if it exists
+    auto issue_iter = [&](int i) {
+        if (i + NSX - 1 >= 0 && i + NSX - 1 < nk) issue_x(i + NSX - 1);
+        if (i + NSW - 1 >= 0 && i + NSW - 1 < nk) issue_w(i + NSW - 1);
     };
 
-    // ------------------------------------------------------ W stream (registers)
-    const int vhi = max(min(ce, V) - 1, 0);
-    auto w_load = [&](WCursor u) -> WFrags {
-        int kc = kc0 + u.ki;
-        if (kc >= nkc) kc -= nkc;
-        const int k = min(kc * KC + u.s * KSTEP + lgrp * 8, H - 8);
-        const int base = cs + 64 * u.c;
-        WFrags r;
-#pragma unroll
-        for (int fv = 0; fv < 4; ++fv) {
-            const int v = max(min(base + 16 * fv + lrow, vhi), 0);
-            r.f[fv] = load_w(p.w + (size_t)v * rowbytes + (size_t)k * 2);
-        }
-        return r;
-    };
+    // fragment read offsets: row (l & 15) of a 16-row block, chunk 4 s + l / 16 for
+    // K-step s of the stage (the swizzle of row 16 q + lrow is that of lrow)
+    const int lrow = lane & 15;
+    const int lgrp = lane >> 4;
+    const int lswz = chunk_swz<CPR>(lrow);
+    const int frag_off0 = lrow * ROWB + ((lgrp ^ lswz) << 4);
+    const int frag_off1 = lrow * ROWB + ((((4 + lgrp) % CPR) ^ lswz) << 4);
 
     f32x4_t acc[4][FM];
 #pragma unroll
@@ -191,192 +234,161 @@ __global__ __launch_bounds__(512, 1) void wide_kernel(LmHeadArgs p) {
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) acc[fv][fm] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // running statistics of this wave's positions, draft id of each position
-    const float ninf = -__builtin_inff();
-    for (int i = tid; i < 4 * ROWS; i += NT) stats[i] = WStat{ninf, 0.f, ninf, INT_MAX};
-    for (int i = tid; i < ROWS; i += NT) {
-        int d = -1;
-        const int pos = m0 + i;
-        if (i < mrows && p.drafts != nullptr) {
-            if (pos < p.Mt) {
-                const int b = pos / (p.k + 1);
-                const int j = pos - b * (p.k + 1);
-                d = (j < p.k) ? p.drafts[b * p.k + j] : -1;
-            } else {
-                d = p.drafts[pos - p.Mt];
-            }
-        }
-        dtok[i] = d;
-    }
-
-    WFrags wb[PF];
-    WCursor cur{0, 0, 0};
 #pragma unroll
-    for (int i = 0; i < PF; ++i) {
-        wb[i] = w_load(cur);
-        cur = advance(cur, nkc, nch);
-    }
-    x_load(kc0);
-    x_store(xbuf0);
-    __syncthreads();
+    for (int i = -(NSW - 1); i < 0; ++i) issue_iter(i);
 
+    for (int kb = 0; kb < nk; ++kb) {
+        // this wave's loads of stage kb are done when only later ones remain; the
+        // last of those counted, W(kb + NSW - 2), exists iff kb + NSW - 2 < nk
+        if (kb + NSW - 2 < nk) wait_vm<Cfg::WAIT>();
+        else wait_vm<0>();
+        stage_barrier();  // every wave's stage kb landed; stage kb - 1 fully read
+        issue_iter(kb);   // into the buffers stage kb - 1 used
+
+        const uint8_t* wbase = wring + (kb % NSW) * Cfg::WSTAGE + (vw * 64) * ROWB;
+        const uint8_t* xbase = xring + (kb % NSX) * Cfg::XSTAGE + (mw * (BM / 2)) * ROWB;
+#pragma unroll
+        for (int s = 0; s < Cfg::KS; ++s) {
+            const int fo = s == 0 ? frag_off0 : frag_off1;
+            u32x4_t a[4], b[FM];
+#pragma unroll
+            for (int fv = 0; fv < 4; ++fv) a[fv] = *(const u32x4_t*)(wbase + fv * 16 * ROWB + fo);
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) b[fm] = *(const u32x4_t*)(xbase + fm * 16 * ROWB + fo);
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int fv = 0; fv < 4; ++fv)
+                    acc[fv][fm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[fv]),
+                                                                          __builtin_bit_cast(bf16x8_t, b[fm]),
+                                                                          acc[fv][fm], 0, 0, 0);
+        }
+    }
+    __syncthreads();  // all stages read: the LDS is reused for the statistics
+
+    // ------------------------------------------------------------- epilogue
+    WStat* stats = reinterpret_cast<WStat*>(smem);  // [4][BM]
+    const float ninf = -__builtin_inff();
     const float c2 = p.c2;
     const bool vec_spill = (V & 3) == 0;
-
-    // Fold this wave's logits of column chunk c into the running statistics.
-    auto epilogue = [&](int c) {
-        const int vbase = cs + 64 * c;
-        const int vr = min(64, ce - vbase);  // valid rows of this chunk (may be <= 0)
+    const int vbase = v0 + vw * 64;
+    const int vr = min(64, v1 - vbase);  // valid rows of this wave (may be <= 0)
+    const int mrows = min(BM, p.Meff - m0);
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-            const int pl = half * 16 * FM + 16 * fm + lrow;  // position within the chunk
-            const bool pv = pl < mrows;
-            const int pos = m0 + pl;
-            float mx = ninf, bv = ninf;
-            int bi = INT_MAX;
+    for (int fm = 0; fm < FM; ++fm) {
+        const int pl = mw * (BM / 2) + 16 * fm + lrow;  // position within the tile
+        const bool pv = pl < mrows;
+        const int pos = m0 + pl;
+        float mx = ninf, bv = ninf;
+        int bi = INT_MAX;
+#pragma unroll
+        for (int fv = 0; fv < 4; ++fv)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int vo = 16 * fv + 4 * lgrp + t;
+                const float l = acc[fv][fm][t];
+                if (vo < vr) {
+                    mx = fmaxf(mx, l * c2);
+                    if (l > bv) {
+                        bv = l;
+                        bi = vbase + vo;
+                    }
+                }
+            }
+#pragma unroll
+        for (int off = 16; off <= 32; off <<= 1) {
+            mx = fmaxf(mx, __shfl_xor(mx, off));
+            const float obv = __shfl_xor(bv, off);
+            const int obi = __shfl_xor(bi, off);
+            if (obv > bv || (obv == bv && obi < bi)) {
+                bv = obv;
+                bi = obi;
+            }
+        }
+        float s = 0.f;
+        if (mx != ninf) {
 #pragma unroll
             for (int fv = 0; fv < 4; ++fv)
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int vo = 16 * fv + 4 * lgrp + t;
-                    const float l = acc[fv][fm][t];
+                for (int t = 0; t < 4; ++t)
+                    if (16 * fv + 4 * lgrp + t < vr) s += exp2f(acc[fv][fm][t] * c2 - mx);
+        }
+        s += __shfl_xor(s, 16);
+        s += __shfl_xor(s, 32);
+        if (pv) {
+            // draft id of this position: slot j < k of a target row, or a drafter row
+            int d = -1;
+            if (p.drafts != nullptr) {
+                if (pos < p.Mt) {
+                    const int b = pos / (p.k + 1);
+                    const int j = pos - b * (p.k + 1);
+                    if (j < p.k) d = p.drafts[b * p.k + j];
+                } else {
+                    d = p.drafts[pos - p.Mt];
+                }
+            }
+            const int dd = d - vbase;
+            if (dd >= 0 && dd < vr && ((dd >> 2) & 3) == lgrp) {
+                // select the element without a runtime index into the accumulators
+                const int fv = dd >> 4, t = dd & 3;
+                float l = 0.f;
+#pragma unroll
+                for (int f = 0; f < 4; ++f) {
+                    const f32x4_t a = acc[f][fm];
+                    const float e = t == 0 ? a[0] : t == 1 ? a[1] : t == 2 ? a[2] : a[3];
+                    l = (f == fv) ? e : l;
+                }
+                p.dlogit[pos] = l;
+            }
+            if (p.spill != nullptr) {
+#pragma unroll
+                for (int fv = 0; fv < 4; ++fv) {
+                    const int vo = 16 * fv + 4 * lgrp;
                     if (vo < vr) {
-                        mx = fmaxf(mx, l * c2);
-                        if (l > bv) {
-                            bv = l;
-                            bi = vbase + vo;
+                        float* dst = p.spill + (size_t)pos * V + vbase + vo;
+                        if (vec_spill && vo + 3 < vr) {
+                            *(f32x4_t*)dst = acc[fv][fm];
+                        } else {
+#pragma unroll
+                            for (int t = 0; t < 4; ++t)
+                                if (vo + t < vr) dst[t] = acc[fv][fm][t];
                         }
                     }
                 }
-#pragma unroll
-            for (int off = 16; off <= 32; off <<= 1) {
-                mx = fmaxf(mx, __shfl_xor(mx, off));
-                const float obv = __shfl_xor(bv, off);
-                const int obi = __shfl_xor(bi, off);
-                if (obv > bv || (obv == bv && obi < bi)) {
-                    bv = obv;
-                    bi = obi;
-                }
             }
-            float s = 0.f;
-            if (mx != ninf) {
-#pragma unroll
-                for (int fv = 0; fv < 4; ++fv)
-#pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        if (16 * fv + 4 * lgrp + t < vr) s += exp2f(acc[fv][fm][t] * c2 - mx);
-            }
-            s += __shfl_xor(s, 16);
-            s += __shfl_xor(s, 32);
-            if (pv) {
-                // draft logit and fp32 logits of this chunk
-                const int dd = dtok[pl] - vbase;
-                if (dd >= 0 && dd < vr && ((dd >> 2) & 3) == lgrp) {
-                    // select the element without a runtime index into the accumulators
-                    const int fv = dd >> 4, t = dd & 3;
-                    float l = 0.f;
-#pragma unroll
-                    for (int f = 0; f < 4; ++f) {
-                        const f32x4_t a = acc[f][fm];
-                        const float e = t == 0 ? a[0] : t == 1 ? a[1] : t == 2 ? a[2] : a[3];
-                        l = (f == fv) ? e : l;
-                    }
-                    p.dlogit[pos] = l;
-                }
-                if (p.spill != nullptr) {
-#pragma unroll
-                    for (int fv = 0; fv < 4; ++fv) {
-                        const int vo = 16 * fv + 4 * lgrp;
-                        if (vo < vr) {
-                            float* dst = p.spill + (size_t)pos * V + vbase + vo;
-                            if (vec_spill && vo + 3 < vr) {
-                                *(f32x4_t*)dst = acc[fv][fm];
-                            } else {
-#pragma unroll
-                                for (int t = 0; t < 4; ++t)
-                                    if (vo + t < vr) dst[t] = acc[fv][fm][t];
-                            }
-                        }
-                    }
-                }
-                if (lgrp == 0 && mx != ninf) {
-                    WStat& st = stats[wave * ROWS + pl];
-                    st = merge_wstat(st, WStat{mx, s, bv, bi});
-                }
-            }
-#pragma unroll
-            for (int fv = 0; fv < 4; ++fv) acc[fv][fm] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            __builtin_amdgcn_sched_barrier(0);  // one fragment's temporaries at a time
         }
-    };
-
-    for (int it = 0; it < total_it; ++it) {
-        const int c = it / nkc;
-        const int kci = it - c * nkc;
-        {
-            // next K-chunk's hidden states (the last iteration re-stages a valid
-            // chunk nobody reads: no branch around the loads keeps the wait counts exact)
-            int kn = kc0 + (kci + 1 == nkc ? 0 : kci + 1);
-            if (kn >= nkc) kn -= nkc;
-            x_load(kn);
-        }
-        const uint8_t* xb = (it & 1) ? xbuf1 : xbuf0;
-        const int nfv = min(4, max(0, (min(64, ce - (cs + 64 * c)) + 15) / 16));
-#pragma unroll
-        for (int s = 0; s < SPC; ++s) {  // ring slot s holds this step (PF == SPC)
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                const u32x4_t bx =
-                    *(const u32x4_t*)(xb + (half * 16 * FM + 16 * fm + lrow) * PITCH + (s * KSTEP + lgrp * 8) * 2);
-#pragma unroll
-                for (int fv = 0; fv < 4; ++fv)
-                    if (fv < nfv)
-                        acc[fv][fm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8_t, wb[s].f[fv]), __builtin_bit_cast(bf16x8_t, bx), acc[fv][fm], 0,
-                            0, 0);
-            }
-            wb[s] = w_load(cur);
-            cur = advance(cur, nkc, nch);
-        }
-        x_store((it & 1) ? xbuf0 : xbuf1);
-        if (kci == nkc - 1) epilogue(c);
-        __syncthreads();
+        if (lgrp == 0) stats[vw * BM + pl] = WStat{mx, s, bv, bi};
+        __builtin_amdgcn_sched_barrier(0);  // one fragment's temporaries at a time
     }
-
-    // merge the four columns' statistics per position
+    __syncthreads();
     if (tid < mrows) {
         WStat o = stats[tid];
 #pragma unroll
-        for (int w = 1; w < 4; ++w) o = merge_wstat(o, stats[w * ROWS + tid]);
-        p.partials[(size_t)(m0 + tid) * R + rg] = Partial{o.x, o.s, o.bv, o.bi};
+        for (int w = 1; w < 4; ++w) o = merge_wstat(o, stats[w * BM + tid]);
+        p.partials[(size_t)(m0 + tid) * S + vt] = Partial{o.x, o.s, o.bv, o.bi};
     }
 }
 
-template <int FM>
-hipError_t launch_fm(const Plan& plan, const LmHeadArgs& args, hipStream_t stream) {
-    auto kern = wide_kernel<FM>;
+template <int BM>
+hipError_t launch_bm(const Plan& plan, const LmHeadArgs& args, hipStream_t stream) {
+    auto kern = wide_kernel<BM>;
     const size_t lds = plan.lds;
-    if (lds > 64 * 1024) {
-        const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(kern, dim3(plan.grid), dim3(512), lds, stream, args);
+    const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(plan.grid), dim3(NT), lds, stream, args);
     return hipGetLastError();
 }
 
 }  // namespace
 
-size_t wide_lds_bytes(int fm) {
-    const size_t rows = (size_t)32 * fm;
-    return 2 * rows * PITCH + 4 * rows * sizeof(WStat) + rows * sizeof(int);
-}
+int wide_rows() { return BV; }
+
+size_t wide_lds_bytes(int bm) { return bm == 256 ? WideCfg<256>::LDS : WideCfg<128>::LDS; }
 
 hipError_t launch_wide(const Plan& plan, const LmHeadArgs& args, hipStream_t stream) {
     switch (plan.nt) {
-        case 1: return launch_fm<1>(plan, args, stream);
-        case 2: return launch_fm<2>(plan, args, stream);
-        case 3: return launch_fm<3>(plan, args, stream);
-        case 4: return launch_fm<4>(plan, args, stream);
+        case 128: return launch_bm<128>(plan, args, stream);
+        case 256: return launch_bm<256>(plan, args, stream);
         default: return hipErrorInvalidConfiguration;
     }
 }

@@ -30,6 +30,8 @@ SMALL = {
     "k8_f32": (C(H=64, V=300, B=2, k=8, dtype="f32", cid=107), 12),
     "V50_bf16": (C(H=64, V=50, B=3, k=2, cid=108), 12),
     "position_chunks_f32": (C(H=128, V=500, B=8, k=3, dtype="f32", cid=109), 6),
+    "ragged_hidden_many_bf16": (C(H=264, V=1000, B=8, k=3, cid=120), 4),
+    "many_chunks_bf16": (C(H=192, V=700, B=70, k=4, T=0.9, cid=121), 2),
 }
 
 
