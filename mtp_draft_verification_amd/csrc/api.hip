@@ -277,7 +277,10 @@ int run(const Plan& plan, const void* xt, const void* xd, const void* w, const i
     la.spill = spill;
     la.err = err;
     la.tiles = plan.tiles;
-    la.rotate = k_rotate();
+    // The streaming kernels spread their waves over the K order; the wide kernel keeps
+    // every tile at the same K offset so that the tiles running together on an XCD
+    // share their hidden-state and W chunks in L2.
+    la.rotate = plan.kind == KIND_WIDE ? 0 : k_rotate();
 
     std::pair<hipEvent_t, hipEvent_t>* ev = timing_slot();
     if (ev && hipEventRecord(ev->first, stream) != hipSuccess) return MTPV_EDEVICE;

@@ -266,27 +266,37 @@ __device__ __forceinline__ double wave_sum(double v) {
     return v;
 }
 
-// exp(l / T - ref) in fp64 for element v of `row` (0 past V or for row < 0).
-__device__ __forceinline__ double row_exp(const float* logits, int row, int V, int v, double inv_t, double ref) {
-    if (row < 0 || v >= V) return 0.0;
-    const double l = (double)logits[(size_t)row * V + v];
-    return exp(fma(l, inv_t, -ref));
+// Logit of element v of `row` (0 past V or for row < 0; such elements get weight 0).
+__device__ __forceinline__ float row_logit(const float* logits, int row, int V, int v) {
+    return (row < 0 || v >= V) ? 0.f : logits[(size_t)row * V + v];
 }
 
-// Weight of element v for a job: max(0, p - q) with a drafter row, else p.
-__device__ __forceinline__ double job_weight(const float* logits, const Job& job, bool use_q, int V, int v,
-                                             double inv_t, double zp, double zq) {
-    const double pv = row_exp(logits, job.row_p, V, v, inv_t, job.ref_p) / zp;
+// exp(l / T - ref) in fp64 (0 for an element outside the row).
+__device__ __forceinline__ double row_exp_of(float l, bool live, double inv_t, double ref) {
+    return live ? exp(fma((double)l, inv_t, -ref)) : 0.0;
+}
+
+// Weight of one element for a job from its two logits: max(0, p - q) with a drafter
+// row, else p; rp and rq are the reciprocals of the rows' normalisers.
+__device__ __forceinline__ double weight_of(float lp, float lq, bool live, bool use_q, double inv_t, const Job& job,
+                                            double rp, double rq) {
+    const double pv = row_exp_of(lp, live, inv_t, job.ref_p) * rp;
     if (!use_q) return pv;
-    const double qv = row_exp(logits, job.row_q, V, v, inv_t, job.ref_q) / zq;
+    const double qv = row_exp_of(lq, live, inv_t, job.ref_q) * rq;
     const double d = pv - qv;
     return d > 0.0 ? d : 0.0;
 }
 
-// Inclusive scan over one 64-token tile, lane i holding token tile*64 + i.
-__device__ __forceinline__ double tile_scan(const float* logits, const Job& job, bool use_q, int V, int tile,
-                                            double inv_t, double zp, double zq, int lane) {
-    double x = job_weight(logits, job, use_q, V, tile * 64 + lane, inv_t, zp, zq);
+__device__ __forceinline__ double job_weight(const float* logits, const Job& job, bool use_q, int V, int v,
+                                             double inv_t, double rp, double rq) {
+    const float lp = row_logit(logits, job.row_p, V, v);
+    const float lq = use_q ? row_logit(logits, job.row_q, V, v) : 0.f;
+    return weight_of(lp, lq, v < V, use_q, inv_t, job, rp, rq);
+}
+
+// Inclusive scan of one 64-token tile's weights in lane order, lane i holding the
+// weight of token tile * 64 + i.
+__device__ __forceinline__ double lane_scan(double x, int lane) {
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
         const double y = __shfl_up(x, off);
@@ -295,30 +305,53 @@ __device__ __forceinline__ double tile_scan(const float* logits, const Job& job,
     return x;
 }
 
-__device__ __forceinline__ void normalisers(const ResidualArgs& p, int j, double* zp, double* zq) {
+__device__ __forceinline__ double tile_scan(const float* logits, const Job& job, bool use_q, int V, int tile,
+                                            double inv_t, double rp, double rq, int lane) {
+    return lane_scan(job_weight(logits, job, use_q, V, tile * 64 + lane, inv_t, rp, rq), lane);
+}
+
+// Reciprocals of the job's normalisers (sums of the fixed-order chunk partials).
+__device__ __forceinline__ void normalisers(const ResidualArgs& p, int j, double* rp, double* rq) {
     double a = 0.0, b = 0.0;
     const double* zpart = p.zpart + (size_t)j * p.C * 2;
     for (int c = 0; c < p.C; ++c) {
         a += zpart[2 * c];
         b += zpart[2 * c + 1];
     }
-    *zp = a;
-    *zq = b;
+    *rp = 1.0 / a;
+    *rq = 1.0 / b;
 }
+
+// Tokens per thread and loop trip in the sampling passes: the loads of all of them
+// are issued before the fp64 arithmetic, so each thread keeps 2 * UR loads in flight.
+constexpr int UR = 8;
 
 // Pass 1: per-chunk sums of exp(l/T - ref) for the job's p row and q row.
 __global__ __launch_bounds__(256) void zsum_kernel(ResidualArgs p) {
     __shared__ double sh[2][4];
     const int j = blockIdx.y, c = blockIdx.x;
     const Job job = p.jobs[j];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int tpc = (p.ntiles + p.C - 1) / p.C;
     const int t0 = c * tpc, t1 = min(p.ntiles, t0 + tpc);
+    const int e1 = min(p.V, t1 * 64);
+    const bool has_q = job.row_q >= 0;
     double sp = 0.0, sq = 0.0;
-    for (int t = t0 + wave; t < t1; t += 4) {
-        const int v = t * 64 + lane;
-        sp += row_exp(p.logits, job.row_p, p.V, v, p.inv_t, job.ref_p);
-        sq += row_exp(p.logits, job.row_q, p.V, v, p.inv_t, job.ref_q);
+    for (int base = t0 * 64; base < e1; base += 256 * UR) {
+        float lp[UR], lq[UR];
+#pragma unroll
+        for (int i = 0; i < UR; ++i) {
+            const int v = base + 256 * i + tid;
+            lp[i] = v < e1 ? row_logit(p.logits, job.row_p, p.V, v) : 0.f;
+            lq[i] = v < e1 ? row_logit(p.logits, job.row_q, p.V, v) : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < UR; ++i) {
+            const bool live = base + 256 * i + tid < e1;
+            sp += row_exp_of(lp[i], live && job.row_p >= 0, p.inv_t, job.ref_p);
+            sq += row_exp_of(lq[i], live && has_q, p.inv_t, job.ref_q);
+        }
     }
     sp = wave_sum(sp);
     sq = wave_sum(sq);
@@ -327,26 +360,42 @@ __global__ __launch_bounds__(256) void zsum_kernel(ResidualArgs p) {
         sh[1][wave] = sq;
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (tid == 0) {
         double* out = p.zpart + ((size_t)j * p.C + c) * 2;
         out[0] = ((sh[0][0] + sh[0][1]) + sh[0][2]) + sh[0][3];
         out[1] = ((sh[1][0] + sh[1][1]) + sh[1][2]) + sh[1][3];
     }
 }
 
-// Pass 2: per-tile sums of the job's weights.
+// Pass 2: per-tile sums of the job's weights (the lane-order scan's last value, the
+// same arithmetic the search pass repeats on the tile it lands in).
 __global__ __launch_bounds__(256) void tsum_kernel(ResidualArgs p) {
     const int j = blockIdx.y, c = blockIdx.x;
     const Job job = p.jobs[j];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    double zp, zq;
-    normalisers(p, j, &zp, &zq);
+    double rp, rq;
+    normalisers(p, j, &rp, &rq);
     const bool use_q = job.row_q >= 0;
     const int tpc = (p.ntiles + p.C - 1) / p.C;
     const int t0 = c * tpc, t1 = min(p.ntiles, t0 + tpc);
-    for (int t = t0 + wave; t < t1; t += 4) {
-        const double incl = tile_scan(p.logits, job, use_q, p.V, t, p.inv_t, zp, zq, lane);
-        if (lane == 63) p.tsum[(size_t)j * p.ntiles + t] = incl;
+    for (int tb = t0 + wave; tb < t1; tb += 4 * UR) {
+        float lp[UR], lq[UR];
+#pragma unroll
+        for (int i = 0; i < UR; ++i) {
+            const int t = tb + 4 * i;
+            const int v = t * 64 + lane;
+            lp[i] = t < t1 ? row_logit(p.logits, job.row_p, p.V, v) : 0.f;
+            lq[i] = (t < t1 && use_q) ? row_logit(p.logits, job.row_q, p.V, v) : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < UR; ++i) {
+            const int t = tb + 4 * i;
+            if (t < t1) {  // uniform over the wave
+                const double w = weight_of(lp[i], lq[i], t * 64 + lane < p.V, use_q, p.inv_t, job, rp, rq);
+                const double incl = lane_scan(w, lane);
+                if (lane == 63) p.tsum[(size_t)j * p.ntiles + t] = incl;
+            }
+        }
     }
 }
 
@@ -361,8 +410,8 @@ __global__ __launch_bounds__(256) void search_kernel(ResidualArgs p) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const Job job = p.jobs[j];
-    double zp, zq;
-    normalisers(p, j, &zp, &zq);
+    double rp, rq;
+    normalisers(p, j, &rp, &rq);
     bool use_q = job.row_q >= 0;
     double* ts = p.tsum + (size_t)j * p.ntiles;
     const int per = (p.ntiles + 255) / 256;
@@ -371,7 +420,7 @@ __global__ __launch_bounds__(256) void search_kernel(ResidualArgs p) {
         if (pass == 1) {
             // Residual mass was zero: draw from p instead (tile sums rebuilt for p).
             for (int t = wave; t < p.ntiles; t += 4) {
-                const double incl = tile_scan(p.logits, job, false, p.V, t, p.inv_t, zp, zq, lane);
+                const double incl = tile_scan(p.logits, job, false, p.V, t, p.inv_t, rp, rq, lane);
                 if (lane == 63) ts[t] = incl;
             }
             __syncthreads();
@@ -436,8 +485,8 @@ __global__ __launch_bounds__(256) void search_kernel(ResidualArgs p) {
             continue;
         }
         if (wave == 0) {
-            const double incl = tile_scan(p.logits, job, use_q, p.V, sh_tile, p.inv_t, zp, zq, lane);
-            const double w = job_weight(p.logits, job, use_q, p.V, sh_tile * 64 + lane, p.inv_t, zp, zq);
+            const double incl = tile_scan(p.logits, job, use_q, p.V, sh_tile, p.inv_t, rp, rq, lane);
+            const double w = job_weight(p.logits, job, use_q, p.V, sh_tile * 64 + lane, p.inv_t, rp, rq);
             const unsigned long long hit = __ballot(sh_base + incl > sh_target);
             const unsigned long long pos = __ballot(w > 0.0);
             int ln;

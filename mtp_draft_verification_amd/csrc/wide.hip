@@ -164,7 +164,8 @@ __global__ __launch_bounds__(512, 1) void wide_kernel(LmHeadArgs p) {
     const int m0 = mt * BM;
     const int nk = (H + BK - 1) / BK;
     const size_t rowbytes = (size_t)H * 2;
-    // the position chunks of one vocabulary tile share its rotation (and its W in L2)
+    // optional rotation of the K order per vocabulary tile (the position chunks of
+    // one tile share it, and so their W in L2)
     const int kb0 = p.rotate ? (int)(((unsigned)vt * 7u) % (unsigned)nk) : 0;
 
     // ------------------------------------------------------------ stage loads
