@@ -34,7 +34,8 @@ from the last target distribution. Random numbers come from Philox4x32-10
 Layers:
   numerics  (fp64)        : decode_bf16, lm_head_logits, softmax
   decision rule           : greedy_verify, stochastic_verify, inverse_cdf,
-                            residual_weights, sample_drafts
+                            residual_weights, sample_drafts,
+                            greedy_verify_ragged, stochastic_verify_ragged
   random numbers          : philox.philox4x32_10, philox.verify_uniforms
   metrics                 : metrics.acceptance_metrics
 
@@ -56,6 +57,10 @@ from .verify import (
     verify_greedy_from_hidden,
     verify_sample_from_hidden,
     draft_from_hidden,
+    greedy_verify_ragged,
+    stochastic_verify_ragged,
+    verify_greedy_ragged_from_hidden,
+    verify_sample_ragged_from_hidden,
 )
 from .philox import philox4x32_10, uniform24, verify_uniforms
 from .metrics import acceptance_metrics
@@ -64,5 +69,7 @@ __all__ = [
     "decode_bf16", "lm_head_logits", "softmax", "greedy_verify",
     "residual_weights", "inverse_cdf", "stochastic_verify", "sample_drafts",
     "verify_greedy_from_hidden", "verify_sample_from_hidden", "draft_from_hidden",
+    "greedy_verify_ragged", "stochastic_verify_ragged", "verify_greedy_ragged_from_hidden",
+    "verify_sample_ragged_from_hidden",
     "philox4x32_10", "uniform24", "verify_uniforms", "acceptance_metrics",
 ]

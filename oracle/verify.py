@@ -213,6 +213,50 @@ def sample_drafts(Q, u_draft):
     return tok.reshape(B, k).astype(np.int32)
 
 
+# ------------------------------------------------------- ragged draft lengths
+
+def greedy_verify_ragged(Lt, drafts, klen):
+    """Greedy verification when request b proposes only its first klen[b] <= k drafts.
+
+    Dynamic draft length is named as coming drafter support ("Faster Rollouts with
+    MTP Speculative Decoding", section "What's Next"); the pages give no rule for
+    it. Reading: a request with k_b drafts is verified exactly as a call with k =
+    k_b would verify it (target rows 0..k_b, bonus at slot k_b); its output row is
+    then padded with -1 to k + 1 slots. Drafts at slots >= k_b are ignored.
+    """
+    Lt = np.asarray(Lt)
+    drafts = np.asarray(drafts, dtype=np.int64)
+    B, k1, _ = Lt.shape
+    a = np.zeros(B, dtype=np.int64)
+    out = np.full((B, k1), -1, dtype=np.int32)
+    for b in range(B):
+        kb = int(klen[b])
+        ab, ob, _ = greedy_verify(Lt[b:b + 1, :kb + 1], drafts[b:b + 1, :kb])
+        a[b] = ab[0]
+        out[b, :kb + 1] = ob[0]
+    return a, out
+
+
+def stochastic_verify_ragged(P, Q, drafts, klen, u_acc, u_res):
+    """Stochastic verification with per-request draft counts klen[b] <= k.
+
+    Same reading as greedy_verify_ragged: request b runs the exact rule of
+    stochastic_verify on its first k_b slots (p_0..p_kb, q_0..q_(kb-1), uniforms
+    of slots 0..k_b), so after k_b acceptances the bonus comes from p_kb.
+    """
+    drafts = np.asarray(drafts, dtype=np.int64)
+    B, k = drafts.shape
+    a = np.zeros(B, dtype=np.int64)
+    out = np.full((B, k + 1), -1, dtype=np.int32)
+    for b in range(B):
+        kb = int(klen[b])
+        ab, ob, _ = stochastic_verify(P[b:b + 1, :kb + 1], Q[b:b + 1, :kb], drafts[b:b + 1, :kb],
+                                      u_acc[b:b + 1, :kb], u_res[b:b + 1, :kb + 1])
+        a[b] = ab[0]
+        out[b, :kb + 1] = ob[0]
+    return a, out
+
+
 # -------------------------------------------------------------- whole verify calls
 
 def verify_greedy_from_hidden(Xt, W, drafts):
@@ -235,6 +279,28 @@ def verify_sample_from_hidden(Xt, Xd, W, drafts, T, seed, step, b0=0):
     u_acc, u_res, _ = verify_uniforms(seed, step, B, k, b0)
     a, out, diag = stochastic_verify(P, Q, drafts, u_acc, u_res)
     return {"a": a, "out": out, "Lt": Lt, "Ld": Ld, "P": P, "Q": Q, **diag}
+
+
+def verify_greedy_ragged_from_hidden(Xt, W, drafts, klen):
+    """Greedy verify call with per-request draft counts (see greedy_verify_ragged)."""
+    Lt = lm_head_logits(Xt, W)
+    a, out = greedy_verify_ragged(Lt, drafts, klen)
+    return {"a": a, "out": out, "Lt": Lt}
+
+
+def verify_sample_ragged_from_hidden(Xt, Xd, W, drafts, klen, T, seed, step, b0=0):
+    """Stochastic verify call with per-request draft counts; uniforms as in
+    verify_sample_from_hidden (slot j, request b)."""
+    from .philox import verify_uniforms
+    drafts = np.asarray(drafts)
+    B, k = drafts.shape
+    Lt = lm_head_logits(Xt, W)
+    Ld = lm_head_logits(Xd, W) if k > 0 else np.zeros((B, 0, Lt.shape[-1]))
+    P = softmax(Lt, T)
+    Q = softmax(Ld, T) if k > 0 else Ld
+    u_acc, u_res, _ = verify_uniforms(seed, step, B, k, b0)
+    a, out = stochastic_verify_ragged(P, Q, drafts, klen, u_acc, u_res)
+    return {"a": a, "out": out, "Lt": Lt, "Ld": Ld, "P": P, "Q": Q}
 
 
 def draft_from_hidden(Xd, W, T, seed, step, b0=0):
