@@ -75,6 +75,7 @@ typedef enum mtpv_mode { MTPV_MODE_GREEDY = 0, MTPV_MODE_SAMPLE = 1, MTPV_MODE_D
 
 /* Bits of the per-call device error word. */
 #define MTPV_DEVERR_DRAFT_RANGE 1 /* some draft id was outside [0, V); it was rejected */
+#define MTPV_DEVERR_DRAFT_LEN 2   /* some draft_len[b] was outside [0, k]; it was clamped */
 
 /*
  * Optional exports for parity tests; pass NULL (or NULL members) in production.
@@ -170,6 +171,53 @@ MTPV_API int spec_verify_sample(const void* target_hidden, const void* draft_hid
                        const int32_t* draft_tokens, int B, int k, int H, int V, int dtype,
                        double temperature, uint64_t seed, uint64_t offset,
                        int32_t* accepted_len, int32_t* out_tokens,
+                       void* workspace, size_t workspace_bytes,
+                       const mtpv_debug* debug, void* stream);
+
+/*
+ * Verification with a draft count per request ("dynamic draft length", named as
+ * coming drafter support in "Faster Rollouts with MTP Speculative Decoding",
+ * section "What's Next"; the pages give no rule, the reading is this one):
+ * request b proposed only its first k_b = draft_len[b] drafts, 0 <= k_b <= k, and
+ * is verified exactly as a call with k = k_b would verify it: slots 0..k_b-1 are
+ * judged, a <= k_b, after k_b acceptances the bonus comes from target row k_b
+ * (p_kb), and out_tokens[b*(k+1) + j] = -1 for j > a. Layouts keep the stride
+ * k: hidden / target_hidden [B, k+1, H], draft_hidden [B, k, H], draft_tokens
+ * [B, k]; rows and drafts past k_b are not used (drafts there may hold any
+ * value). draft_len [B] int32 on the device, or NULL for k_b = k everywhere; a
+ * value outside [0, k] is clamped into it and sets MTPV_DEVERR_DRAFT_LEN.
+ * Philox uniforms as in spec_verify_sample (slot j, request b). Workspace,
+ * debug exports and errors as for spec_verify_greedy / spec_verify_sample.
+ */
+MTPV_API int spec_verify_greedy_ragged(const void* hidden, const void* W_lm, const int32_t* draft_tokens,
+                       const int32_t* draft_len, int B, int k, int H, int V, int dtype,
+                       int32_t* accepted_len, int32_t* out_tokens,
+                       void* workspace, size_t workspace_bytes,
+                       const mtpv_debug* debug, void* stream);
+MTPV_API int spec_verify_sample_ragged(const void* target_hidden, const void* draft_hidden, const void* W_lm,
+                       const int32_t* draft_tokens, const int32_t* draft_len, int B, int k, int H, int V,
+                       int dtype, double temperature, uint64_t seed, uint64_t offset,
+                       int32_t* accepted_len, int32_t* out_tokens,
+                       void* workspace, size_t workspace_bytes,
+                       const mtpv_debug* debug, void* stream);
+
+/*
+ * Greedy and stochastic verification of the same drafts from one pass over W_lm
+ * (both outcomes for A/B acceptance metrics, "Faster Rollouts with MTP
+ * Speculative Decoding", section "Monitoring acceptance"): the head runs once
+ * over the target and drafter rows as in spec_verify_sample; then
+ * accepted_len_greedy / out_tokens_greedy are exactly what spec_verify_greedy
+ * returns for (target_hidden, draft_tokens) and accepted_len_sample /
+ * out_tokens_sample exactly what spec_verify_sample returns. draft_len as in
+ * spec_verify_sample_ragged (NULL = k everywhere). The four output arrays must
+ * not overlap. Workspace: mtpv_workspace_bytes(MTPV_MODE_SAMPLE, ...). Debug
+ * exports are those of the stochastic pass.
+ */
+MTPV_API int spec_verify_dual(const void* target_hidden, const void* draft_hidden, const void* W_lm,
+                       const int32_t* draft_tokens, const int32_t* draft_len, int B, int k, int H, int V,
+                       int dtype, double temperature, uint64_t seed, uint64_t offset,
+                       int32_t* accepted_len_greedy, int32_t* out_tokens_greedy,
+                       int32_t* accepted_len_sample, int32_t* out_tokens_sample,
                        void* workspace, size_t workspace_bytes,
                        const mtpv_debug* debug, void* stream);
 

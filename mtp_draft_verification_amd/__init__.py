@@ -10,6 +10,9 @@ Calls (names as in the C ABI):
   spec_verify_sample(target_hidden, draft_hidden[B,k,H], W, drafts, temperature, seed, offset,
                      accepted_len, out_tokens, workspace)
   spec_draft_sample(draft_hidden[B,kd,H], W, temperature, seed, offset, depth0, draft_tokens[B,kd], workspace)
+  spec_verify_greedy_ragged / spec_verify_sample_ragged(..., draft_len[B], ...)  per-request draft counts
+  spec_verify_dual(target_hidden, draft_hidden, W, drafts, draft_len, temperature, seed, offset,
+                   accepted_len_greedy, out_tokens_greedy, accepted_len_sample, out_tokens_sample, workspace)
 """
 import ctypes
 import os
@@ -20,6 +23,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libmtpv.so")
 MODE_GREEDY, MODE_SAMPLE, MODE_DRAFT = 0, 1, 2
 DTYPE_BF16, DTYPE_F32 = 0, 1
 DEVERR_DRAFT_RANGE = 1
+DEVERR_DRAFT_LEN = 2
 
 STATUS = {0: "MTPV_OK", -1: "MTPV_EINVAL", -2: "MTPV_EALIGN", -3: "MTPV_EWORKSPACE", -4: "MTPV_EDTYPE",
           -5: "MTPV_ENULL", -6: "MTPV_ELAUNCH", -7: "MTPV_EDEVICE"}
@@ -51,6 +55,11 @@ _SIGNATURES = {
     "spec_verify_sample": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _d, _u64, _u64, _vp, _vp, _vp, _sz,
                                 _vp, _vp]),
     "spec_draft_sample": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _d, _u64, _u64, _vp, _vp, _sz, _vp, _vp]),
+    "spec_verify_greedy_ragged": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _sz, _vp, _vp]),
+    "spec_verify_sample_ragged": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _d, _u64, _u64, _vp, _vp,
+                                       _vp, _sz, _vp, _vp]),
+    "spec_verify_dual": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _d, _u64, _u64, _vp, _vp, _vp, _vp,
+                              _vp, _sz, _vp, _vp]),
     "mtpv_device_error": (_i, [_vp, ctypes.POINTER(ctypes.c_int32), _vp]),
     "mtpv_timing_enable": (_i, [_i]),
     "mtpv_timing_read": (_i, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), _i]),
@@ -166,6 +175,53 @@ def spec_verify_sample(target_hidden, draft_hidden, W, drafts, temperature, seed
                                   int(offset) & (2**64 - 1), _ptr(accepted_len), _ptr(out_tokens),
                                   _ptr(workspace), workspace.numel(), _dbg(debug), _stream(stream))
     _check(st, "spec_verify_sample")
+
+
+def spec_verify_greedy_ragged(hidden, W, drafts, draft_len, accepted_len, out_tokens, workspace, debug=None,
+                              stream=None):
+    """Greedy verify with draft_len [B] int32 (k_b <= k drafts per request; None = all k)."""
+    B, k1, H = hidden.shape
+    V = W.shape[0]
+    for n, t in (("hidden", hidden), ("W", W), ("drafts", drafts), ("draft_len", draft_len),
+                 ("workspace", workspace)):
+        _contig(n, t)
+    st = lib().spec_verify_greedy_ragged(_ptr(hidden), _ptr(W), _ptr(drafts), _ptr(draft_len), B, k1 - 1, H, V,
+                                         _dtype_code(W), _ptr(accepted_len), _ptr(out_tokens), _ptr(workspace),
+                                         workspace.numel(), _dbg(debug), _stream(stream))
+    _check(st, "spec_verify_greedy_ragged")
+
+
+def spec_verify_sample_ragged(target_hidden, draft_hidden, W, drafts, draft_len, temperature, seed, offset,
+                              accepted_len, out_tokens, workspace, debug=None, stream=None):
+    """Stochastic verify with draft_len [B] int32 (k_b <= k drafts per request; None = all k)."""
+    B, k1, H = target_hidden.shape
+    V = W.shape[0]
+    for n, t in (("target_hidden", target_hidden), ("draft_hidden", draft_hidden), ("W", W),
+                 ("drafts", drafts), ("draft_len", draft_len), ("workspace", workspace)):
+        _contig(n, t)
+    st = lib().spec_verify_sample_ragged(_ptr(target_hidden), _ptr(draft_hidden), _ptr(W), _ptr(drafts),
+                                         _ptr(draft_len), B, k1 - 1, H, V, _dtype_code(W), float(temperature),
+                                         int(seed) & (2**64 - 1), int(offset) & (2**64 - 1), _ptr(accepted_len),
+                                         _ptr(out_tokens), _ptr(workspace), workspace.numel(), _dbg(debug),
+                                         _stream(stream))
+    _check(st, "spec_verify_sample_ragged")
+
+
+def spec_verify_dual(target_hidden, draft_hidden, W, drafts, draft_len, temperature, seed, offset,
+                     accepted_len_greedy, out_tokens_greedy, accepted_len_sample, out_tokens_sample, workspace,
+                     debug=None, stream=None):
+    """Greedy and stochastic outcomes of the same drafts from one pass over W (sample-mode workspace)."""
+    B, k1, H = target_hidden.shape
+    V = W.shape[0]
+    for n, t in (("target_hidden", target_hidden), ("draft_hidden", draft_hidden), ("W", W),
+                 ("drafts", drafts), ("draft_len", draft_len), ("workspace", workspace)):
+        _contig(n, t)
+    st = lib().spec_verify_dual(_ptr(target_hidden), _ptr(draft_hidden), _ptr(W), _ptr(drafts), _ptr(draft_len),
+                                B, k1 - 1, H, V, _dtype_code(W), float(temperature), int(seed) & (2**64 - 1),
+                                int(offset) & (2**64 - 1), _ptr(accepted_len_greedy), _ptr(out_tokens_greedy),
+                                _ptr(accepted_len_sample), _ptr(out_tokens_sample), _ptr(workspace),
+                                workspace.numel(), _dbg(debug), _stream(stream))
+    _check(st, "spec_verify_dual")
 
 
 def spec_draft_sample(draft_hidden, W, temperature, seed, offset, depth0, draft_tokens, workspace, debug=None,

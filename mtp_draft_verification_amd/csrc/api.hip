@@ -240,9 +240,12 @@ int check_debug(const Plan& plan, const mtpv_debug* dbg) {
     return MTPV_OK;
 }
 
+// One call: the LM-head launch, the decision pass (two passes for the dual call,
+// greedy first, into alen_g / out_g), and the sampling passes.
 int run(const Plan& plan, const void* xt, const void* xd, const void* w, const int32_t* drafts,
-        double temperature, uint64_t seed, uint64_t offset, int depth0, int32_t* alen, int32_t* out,
-        void* ws, const mtpv_debug* dbg, hipStream_t stream) {
+        const int32_t* draft_len, double temperature, uint64_t seed, uint64_t offset, int depth0,
+        int32_t* alen, int32_t* out, void* ws, const mtpv_debug* dbg, hipStream_t stream,
+        int32_t* alen_g = nullptr, int32_t* out_g = nullptr) {
     uint8_t* base = static_cast<uint8_t*>(ws);
     int32_t* err = reinterpret_cast<int32_t*>(base + plan.off_err);
     Partial* partials = reinterpret_cast<Partial*>(base + plan.off_partials);
@@ -294,6 +297,7 @@ int run(const Plan& plan, const void* xt, const void* xd, const void* w, const i
     da.partials = partials;
     da.dlogit = dlogit;
     da.drafts = plan.mode == MTPV_MODE_DRAFT ? nullptr : drafts;
+    da.draft_len = plan.mode == MTPV_MODE_DRAFT ? nullptr : draft_len;
     da.mode = plan.mode;
     da.B = plan.B;
     da.k = plan.k;
@@ -314,6 +318,17 @@ int run(const Plan& plan, const void* xt, const void* xd, const void* w, const i
     da.dbg_pdqd = (dbg && plan.mode != MTPV_MODE_DRAFT) ? dbg->pd_qd : nullptr;
     da.dbg_argmax = dbg ? dbg->argmax : nullptr;
     da.dbg_rowstats = dbg ? dbg->row_stats : nullptr;
+    if (alen_g != nullptr) {
+        // the greedy outcome of the same pass: decisions on the target rows only
+        DecideArgs dg = da;
+        dg.mode = MTPV_MODE_GREEDY;
+        dg.accepted_len = alen_g;
+        dg.out_tokens = out_g;
+        dg.dbg_pdqd = nullptr;
+        dg.dbg_argmax = nullptr;
+        dg.dbg_rowstats = nullptr;
+        if (launch_decide(plan, dg, stream) != hipSuccess) return MTPV_ELAUNCH;
+    }
     if (launch_decide(plan, da, stream) != hipSuccess) return MTPV_ELAUNCH;
 
     if (plan.NJ > 0) {
@@ -389,8 +404,22 @@ int spec_verify_greedy(const void* hidden, const void* W_lm, const int32_t* draf
                           accepted_len, out_tokens, workspace, workspace_bytes, &p);
     if (st == MTPV_OK) st = check_debug(p, debug);
     if (st != MTPV_OK) return st;
-    return run(p, hidden, nullptr, W_lm, draft_tokens, 1.0, 0, 0, 0, accepted_len, out_tokens, workspace, debug,
-               static_cast<hipStream_t>(stream));
+    return run(p, hidden, nullptr, W_lm, draft_tokens, nullptr, 1.0, 0, 0, 0, accepted_len, out_tokens, workspace,
+               debug, static_cast<hipStream_t>(stream));
+}
+
+int spec_verify_greedy_ragged(const void* hidden, const void* W_lm, const int32_t* draft_tokens,
+                              const int32_t* draft_len, int B, int k, int H, int V, int dtype,
+                              int32_t* accepted_len, int32_t* out_tokens, void* workspace, size_t workspace_bytes,
+                              const mtpv_debug* debug, void* stream) {
+    Plan p;
+    int st = common_check(MTPV_MODE_GREEDY, B, k, H, V, dtype, 1.0, hidden, nullptr, W_lm, draft_tokens,
+                          accepted_len, out_tokens, workspace, workspace_bytes, &p);
+    if (st == MTPV_OK && draft_len && !aligned(draft_len, 4)) st = MTPV_EALIGN;
+    if (st == MTPV_OK) st = check_debug(p, debug);
+    if (st != MTPV_OK) return st;
+    return run(p, hidden, nullptr, W_lm, draft_tokens, draft_len, 1.0, 0, 0, 0, accepted_len, out_tokens,
+               workspace, debug, static_cast<hipStream_t>(stream));
 }
 
 int spec_verify_sample(const void* target_hidden, const void* draft_hidden, const void* W_lm,
@@ -402,8 +431,41 @@ int spec_verify_sample(const void* target_hidden, const void* draft_hidden, cons
                           draft_tokens, accepted_len, out_tokens, workspace, workspace_bytes, &p);
     if (st == MTPV_OK) st = check_debug(p, debug);
     if (st != MTPV_OK) return st;
-    return run(p, target_hidden, draft_hidden, W_lm, draft_tokens, temperature, seed, offset, 0, accepted_len,
-               out_tokens, workspace, debug, static_cast<hipStream_t>(stream));
+    return run(p, target_hidden, draft_hidden, W_lm, draft_tokens, nullptr, temperature, seed, offset, 0,
+               accepted_len, out_tokens, workspace, debug, static_cast<hipStream_t>(stream));
+}
+
+int spec_verify_sample_ragged(const void* target_hidden, const void* draft_hidden, const void* W_lm,
+                              const int32_t* draft_tokens, const int32_t* draft_len, int B, int k, int H, int V,
+                              int dtype, double temperature, uint64_t seed, uint64_t offset,
+                              int32_t* accepted_len, int32_t* out_tokens, void* workspace, size_t workspace_bytes,
+                              const mtpv_debug* debug, void* stream) {
+    Plan p;
+    int st = common_check(MTPV_MODE_SAMPLE, B, k, H, V, dtype, temperature, target_hidden, draft_hidden, W_lm,
+                          draft_tokens, accepted_len, out_tokens, workspace, workspace_bytes, &p);
+    if (st == MTPV_OK && draft_len && !aligned(draft_len, 4)) st = MTPV_EALIGN;
+    if (st == MTPV_OK) st = check_debug(p, debug);
+    if (st != MTPV_OK) return st;
+    return run(p, target_hidden, draft_hidden, W_lm, draft_tokens, draft_len, temperature, seed, offset, 0,
+               accepted_len, out_tokens, workspace, debug, static_cast<hipStream_t>(stream));
+}
+
+int spec_verify_dual(const void* target_hidden, const void* draft_hidden, const void* W_lm,
+                     const int32_t* draft_tokens, const int32_t* draft_len, int B, int k, int H, int V, int dtype,
+                     double temperature, uint64_t seed, uint64_t offset, int32_t* accepted_len_greedy,
+                     int32_t* out_tokens_greedy, int32_t* accepted_len_sample, int32_t* out_tokens_sample,
+                     void* workspace, size_t workspace_bytes, const mtpv_debug* debug, void* stream) {
+    Plan p;
+    int st = common_check(MTPV_MODE_SAMPLE, B, k, H, V, dtype, temperature, target_hidden, draft_hidden, W_lm,
+                          draft_tokens, accepted_len_sample, out_tokens_sample, workspace, workspace_bytes, &p);
+    if (st == MTPV_OK && (accepted_len_greedy == nullptr || out_tokens_greedy == nullptr)) st = MTPV_ENULL;
+    if (st == MTPV_OK && (!aligned(accepted_len_greedy, 4) || !aligned(out_tokens_greedy, 4))) st = MTPV_EALIGN;
+    if (st == MTPV_OK && draft_len && !aligned(draft_len, 4)) st = MTPV_EALIGN;
+    if (st == MTPV_OK) st = check_debug(p, debug);
+    if (st != MTPV_OK) return st;
+    return run(p, target_hidden, draft_hidden, W_lm, draft_tokens, draft_len, temperature, seed, offset, 0,
+               accepted_len_sample, out_tokens_sample, workspace, debug, static_cast<hipStream_t>(stream),
+               accepted_len_greedy, out_tokens_greedy);
 }
 
 int spec_draft_sample(const void* draft_hidden, const void* W_lm, int B, int kd, int depth0, int H, int V,
@@ -415,8 +477,8 @@ int spec_draft_sample(const void* draft_hidden, const void* W_lm, int B, int kd,
                           draft_tokens, nullptr, nullptr, workspace, workspace_bytes, &p);
     if (st == MTPV_OK) st = check_debug(p, debug);
     if (st != MTPV_OK) return st;
-    return run(p, nullptr, draft_hidden, W_lm, draft_tokens, temperature, seed, offset, depth0, nullptr, nullptr,
-               workspace, debug, static_cast<hipStream_t>(stream));
+    return run(p, nullptr, draft_hidden, W_lm, draft_tokens, nullptr, temperature, seed, offset, depth0, nullptr,
+               nullptr, workspace, debug, static_cast<hipStream_t>(stream));
 }
 
 int mtpv_device_error(const void* workspace, int32_t* err, void* stream) {

@@ -92,6 +92,7 @@ struct DecideArgs {
     const Partial* partials;
     const float* dlogit;
     const int32_t* drafts;  // [B, k] (greedy, sample)
+    const int32_t* draft_len;  // [B] drafts judged per request, or NULL (all k)
     int mode, B, k, V, Mt, Meff, S, depth0;
     float c2f;              // the fp32 constant the epilogue used
     double inv_t;           // 1 / T in fp64

@@ -99,6 +99,13 @@ __global__ __launch_bounds__(256) void decide_kernel(DecideArgs p) {
     const int lane = tid & 63, wave = tid >> 6;
     const int k = p.k;
     const int nrows = p.mode == 0 ? k + 1 : p.mode == 1 ? 2 * k + 1 : k;
+    // drafts judged for this request (k_b <= k; the rest of its rows are unused)
+    int kb = k;
+    if (p.mode != 2 && p.draft_len != nullptr) {
+        const int v = p.draft_len[b];
+        kb = min(max(v, 0), k);
+        if (v != kb && tid == 0) atomicOr(p.err, 2);
+    }
     const float ninf = -__builtin_inff();
 
     // Decision inputs, independent of the row statistics. They are fetched by the
@@ -205,7 +212,7 @@ __global__ __launch_bounds__(256) void decide_kernel(DecideArgs p) {
     if (p.mode == 2) return;
     __syncthreads();
 
-    if (tid < k) {
+    if (tid < kb) {
         const int j = tid;
         const int d = s_draft[j];
         const bool in_range = d >= 0 && d < p.V;
@@ -232,8 +239,8 @@ __global__ __launch_bounds__(256) void decide_kernel(DecideArgs p) {
     }
     __syncthreads();
     if (tid != 0) return;
-    int al = k;
-    for (int j = 0; j < k; ++j)
+    int al = kb;
+    for (int j = 0; j < kb; ++j)
         if (!keep[j]) {
             al = j;
             break;
@@ -249,12 +256,12 @@ __global__ __launch_bounds__(256) void decide_kernel(DecideArgs p) {
     if (p.mode == 1) {
         Job job;
         job.row_p = b * (k + 1) + al;
-        job.row_q = (al < k) ? p.Mt + b * k + al : -1;
+        job.row_q = (al < kb) ? p.Mt + b * k + al : -1;
         job.out_index = b * (k + 1) + al;
         job.pad = 0;
         job.u = slot_uniform(p.seed, p.offset, al, b, 1);
         job.ref_p = rows[al].x * kLn2;
-        job.ref_q = (al < k) ? rows[k + 1 + al].x * kLn2 : 0.0;
+        job.ref_q = (al < kb) ? rows[k + 1 + al].x * kLn2 : 0.0;
         p.jobs[b] = job;
     }
 }

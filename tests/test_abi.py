@@ -111,3 +111,35 @@ def test_calls_reject_bad_arguments_before_touching_the_device():
                              ctypes.c_void_p(A), ctypes.c_void_p(WS), 1 << 30, None, None)
     assert st == -1
     assert L.mtpv_copy_bytes(ctypes.c_void_p(A), ctypes.c_void_p(A + 4), 16, None) == -2
+
+
+def test_ragged_and_dual_calls_validate_on_the_host():
+    """The per-request-length and dual entry points return the host-side errors (bad
+    sizes, NULL or misaligned draft_len / greedy outputs, small workspace) without
+    enqueueing anything."""
+    L = mv.lib()
+    vp = ctypes.c_void_p
+    ws_small = 1024
+    # invalid B
+    assert L.spec_verify_greedy_ragged(vp(A), vp(A), vp(A), vp(A), 0, 3, 256, 1000, 0, vp(A), vp(A), vp(WS),
+                                       1 << 30, None, None) == -1
+    # misaligned draft_len
+    assert L.spec_verify_greedy_ragged(vp(A), vp(A), vp(A), vp(A + 2), 2, 3, 256, 1000, 0, vp(A), vp(A), vp(WS),
+                                       1 << 30, None, None) == -2
+    # workspace too small
+    assert L.spec_verify_greedy_ragged(vp(A), vp(A), vp(A), None, 2, 3, 256, 1000, 0, vp(A), vp(A), vp(WS),
+                                       ws_small, None, None) == -3
+    # non-positive temperature
+    assert L.spec_verify_sample_ragged(vp(A), vp(A), vp(A), vp(A), vp(A), 2, 3, 256, 1000, 0, 0.0, 0, 0, vp(A),
+                                       vp(A), vp(WS), 1 << 30, None, None) == -1
+    assert L.spec_verify_sample_ragged(vp(A), vp(A), vp(A), vp(A), vp(A + 1), 2, 3, 256, 1000, 0, 1.0, 0, 0,
+                                       vp(A), vp(A), vp(WS), 1 << 30, None, None) == -2
+    # dual: missing greedy outputs, misaligned greedy output, missing drafter rows
+    assert L.spec_verify_dual(vp(A), vp(A), vp(A), vp(A), None, 2, 3, 256, 1000, 0, 1.0, 0, 0, None, vp(A),
+                              vp(A), vp(A), vp(WS), 1 << 30, None, None) == -5
+    assert L.spec_verify_dual(vp(A), vp(A), vp(A), vp(A), None, 2, 3, 256, 1000, 0, 1.0, 0, 0, vp(A + 2), vp(A),
+                              vp(A), vp(A), vp(WS), 1 << 30, None, None) == -2
+    assert L.spec_verify_dual(vp(A), None, vp(A), vp(A), None, 2, 3, 256, 1000, 0, 1.0, 0, 0, vp(A), vp(A),
+                              vp(A), vp(A), vp(WS), 1 << 30, None, None) == -5
+    assert L.spec_verify_dual(vp(A), vp(A), vp(A), vp(A), None, 2, 3, 256, 1000, 0, 1.0, 0, 0, vp(A), vp(A),
+                              vp(A), vp(A), vp(WS), ws_small, None, None) == -3

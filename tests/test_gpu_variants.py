@@ -1,0 +1,218 @@
+"""GPU parity of the verify variants against the oracle, through the C ABI:
+
+* per-request draft counts (spec_verify_greedy_ragged / spec_verify_sample_ragged):
+  random k_b in [0, k] with 0 and k always present, drafts past k_b set to junk
+  (negative and past V) that must be ignored, on a streaming-kernel shape and a
+  tiled-kernel shape; out-of-range lengths are clamped and flagged; a NULL
+  draft_len is the fixed-k call;
+* the dual call (spec_verify_dual): its stochastic outcome equals a separate
+  spec_verify_sample call bit for bit (same kernels), its greedy outcome matches the
+  oracle's greedy rule, also with per-request lengths;
+* a chained drafter loop: one spec_draft_sample call per depth (kd = 1, depth0 =
+  depth) draws the drafts the oracle draws, and the verify call on them matches.
+
+Integer outcomes are compared with the excuse windows of the fixed-k tests, applied
+to each request's first k_b slots.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mtp_draft_verification_amd as mv
+import oracle
+import synth
+from gpu_util import EXCUSE_RATE, Case, compare_outcomes, dev, load_workload, to_dev
+
+pytestmark = pytest.mark.gpu
+
+C = synth.custom
+SHAPES = {
+    "stream": C(H=512, V=5000, B=3, k=3, T=0.8, cid=131),       # greedy 12 rows: streaming kernel
+    "tiled": C(H=256, V=3000, B=24, k=4, T=0.9, cid=130),       # 120 / 216 rows: tiled kernel
+}
+
+
+@pytest.fixture(scope="module")
+def cache():
+    return {}
+
+
+def _weights(cache, wl):
+    if wl.cid not in cache:
+        W_store, W64 = load_workload(wl)
+        cache[wl.cid] = (W_store, W64, to_dev(W_store, wl.dtype))
+    return cache[wl.cid]
+
+
+def _klen(rng, B, k):
+    kl = rng.integers(0, k + 1, size=B).astype(np.int32)
+    kl[0], kl[-1] = 0, k
+    return kl
+
+
+def _junk_past(drafts, klen, V):
+    d = drafts.copy()
+    for b in range(d.shape[0]):
+        for j in range(klen[b], d.shape[1]):
+            d[b, j] = -9 if (b + j) % 2 else V + 5
+    return d
+
+
+def _per_request_oracle(case, mode, drafts, klen, b):
+    """Fixed-k oracle of request b over its first k_b slots (with the window data)."""
+    wl, kb = case.wl, int(klen[b])
+    if mode == "greedy":
+        return oracle.verify_greedy_from_hidden(case.Xt[b:b + 1, :kb + 1], case.W64, drafts[b:b + 1, :kb])
+    return oracle.verify_sample_from_hidden(case.Xt[b:b + 1, :kb + 1], case.Xd[b:b + 1, :kb], case.W64,
+                                            drafts[b:b + 1, :kb], wl.T, wl.seed, case.step, b0=b)
+
+
+def _compare_ragged(case, mode, a, out, drafts, klen):
+    """Checks (a, out) against the ragged oracle; returns (positions, excused)."""
+    wl = case.wl
+    if mode == "greedy":
+        ref = oracle.verify_greedy_ragged_from_hidden(case.Xt, case.W64, drafts, klen)
+    else:
+        ref = oracle.verify_sample_ragged_from_hidden(case.Xt, case.Xd, case.W64, drafts, klen, wl.T, wl.seed,
+                                                      case.step)
+    positions = excused = 0
+    for b in range(wl.B):
+        kb = int(klen[b])
+        assert 0 <= a[b] <= kb
+        assert np.all(out[b, kb + 1:] == -1)
+        assert np.all(ref["out"][b, kb + 1:] == -1)
+        one = _per_request_oracle(case, mode, drafts, klen, b)
+        assert one["a"][0] == ref["a"][b] and np.array_equal(one["out"][0], ref["out"][b, :kb + 1])
+        n, e, fails = compare_outcomes(mode, {"a": a[b:b + 1], "out": out[b:b + 1, :kb + 1]}, one, kb)
+        assert not fails, (b, fails)
+        positions += n
+        excused += e
+    return positions, excused
+
+
+def _call_ragged(case, mode, drafts_d, klen_d):
+    wl = case.wl
+    B, k = wl.B, wl.k
+    alen = torch.full((B,), -7, dtype=torch.int32, device=dev())
+    out = torch.full((B, k + 1), -7, dtype=torch.int32, device=dev())
+    ws = mv.alloc_workspace(mv.MODE_GREEDY if mode == "greedy" else mv.MODE_SAMPLE, B, k, wl.H, wl.V,
+                            mv.DTYPE_BF16, dev())
+    if mode == "greedy":
+        mv.spec_verify_greedy_ragged(case.xt_d, case.W_d, drafts_d, klen_d, alen, out, ws)
+    else:
+        mv.spec_verify_sample_ragged(case.xt_d, case.xd_d, case.W_d, drafts_d, klen_d, case.wl.T, case.wl.seed,
+                                     case.step, alen, out, ws)
+    err = mv.device_error(ws)
+    torch.cuda.synchronize()
+    return alen.cpu().numpy(), out.cpu().numpy(), err
+
+
+@pytest.mark.parametrize("mode", ["greedy", "sample"])
+@pytest.mark.parametrize("shape", list(SHAPES))
+def test_ragged_parity(shape, mode, cache):
+    wl = SHAPES[shape]
+    W_store, W64, Wd = _weights(cache, wl)
+    rng = np.random.default_rng(wl.cid * 10 + (mode == "sample"))
+    positions = excused = 0
+    for step in range(3):
+        print(f"ragged {shape} {mode} step {step}", flush=True)
+        case = Case(wl, W_store, W64, step, Wd)
+        klen = _klen(rng, wl.B, wl.k)
+        drafts = _junk_past(case.drafts, klen, wl.V)
+        a, out, err = _call_ragged(case, mode, torch.from_numpy(drafts).to(dev()), torch.from_numpy(klen).to(dev()))
+        assert err == 0      # junk past k_b is never judged
+        n, e = _compare_ragged(case, mode, a, out, drafts, klen)
+        positions += n
+        excused += e
+    assert excused <= EXCUSE_RATE * positions + 1, (excused, positions)
+
+
+def test_ragged_lengths_out_of_range_are_clamped(cache):
+    wl = SHAPES["tiled"]
+    W_store, W64, Wd = _weights(cache, wl)
+    case = Case(wl, W_store, W64, 0, Wd)
+    klen = np.full(wl.B, 2, dtype=np.int32)
+    klen[1], klen[2] = -3, wl.k + 4
+    for mode in ("greedy", "sample"):
+        a, out, err = _call_ragged(case, mode, case.drafts_d, torch.from_numpy(klen).to(dev()))
+        assert err & mv.DEVERR_DRAFT_LEN
+        clamped = np.clip(klen, 0, wl.k)
+        _compare_ragged(case, mode, a, out, case.drafts, clamped)
+
+
+def test_ragged_null_lengths_equal_fixed_call(cache):
+    wl = SHAPES["tiled"]
+    W_store, W64, Wd = _weights(cache, wl)
+    case = Case(wl, W_store, W64, 1, Wd)
+    B, k = wl.B, wl.k
+    for mode in ("greedy", "sample"):
+        a1, o1, _ = _call_ragged(case, mode, case.drafts_d, None)
+        alen = torch.full((B,), -7, dtype=torch.int32, device=dev())
+        out = torch.full((B, k + 1), -7, dtype=torch.int32, device=dev())
+        ws = mv.alloc_workspace(mv.MODE_GREEDY if mode == "greedy" else mv.MODE_SAMPLE, B, k, wl.H, wl.V,
+                                mv.DTYPE_BF16, dev())
+        if mode == "greedy":
+            mv.spec_verify_greedy(case.xt_d, Wd, case.drafts_d, alen, out, ws)
+        else:
+            mv.spec_verify_sample(case.xt_d, case.xd_d, Wd, case.drafts_d, wl.T, wl.seed, case.step, alen, out, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(a1, alen.cpu().numpy()) and np.array_equal(o1, out.cpu().numpy())
+
+
+@pytest.mark.parametrize("ragged", [False, True])
+@pytest.mark.parametrize("shape", list(SHAPES))
+def test_dual_call(shape, ragged, cache):
+    wl = SHAPES[shape]
+    W_store, W64, Wd = _weights(cache, wl)
+    B, k = wl.B, wl.k
+    rng = np.random.default_rng(wl.cid + 7)
+    positions = excused = 0
+    for step in range(3):
+        print(f"dual {shape} ragged={ragged} step {step}", flush=True)
+        case = Case(wl, W_store, W64, step, Wd)
+        klen = _klen(rng, B, k) if ragged else np.full(B, k, dtype=np.int32)
+        drafts = _junk_past(case.drafts, klen, wl.V) if ragged else case.drafts
+        drafts_d = torch.from_numpy(np.ascontiguousarray(drafts)).to(dev())
+        klen_d = torch.from_numpy(klen).to(dev()) if ragged else None
+        ag = torch.full((B,), -7, dtype=torch.int32, device=dev())
+        og = torch.full((B, k + 1), -7, dtype=torch.int32, device=dev())
+        as_ = torch.full((B,), -7, dtype=torch.int32, device=dev())
+        os_ = torch.full((B, k + 1), -7, dtype=torch.int32, device=dev())
+        ws = mv.alloc_workspace(mv.MODE_SAMPLE, B, k, wl.H, wl.V, mv.DTYPE_BF16, dev())
+        mv.spec_verify_dual(case.xt_d, case.xd_d, Wd, drafts_d, klen_d, wl.T, wl.seed, step, ag, og, as_, os_, ws)
+        assert mv.device_error(ws) == 0
+        # the stochastic outcome is the sample call's, bit for bit
+        a2, o2, _ = _call_ragged(case, "sample", drafts_d, klen_d)
+        assert np.array_equal(as_.cpu().numpy(), a2) and np.array_equal(os_.cpu().numpy(), o2)
+        n, e = _compare_ragged(case, "sample", a2, o2, drafts, klen)
+        positions += n
+        excused += e
+        n, e = _compare_ragged(case, "greedy", ag.cpu().numpy(), og.cpu().numpy(), drafts, klen)
+        positions += n
+        excused += e
+    assert excused <= EXCUSE_RATE * positions + 1, (excused, positions)
+
+
+def test_chained_drafter_loop_then_verify(cache):
+    """k drafter calls, one per depth, then the verify call on what they drew."""
+    wl = SHAPES["tiled"]
+    W_store, W64, Wd = _weights(cache, wl)
+    B, k = wl.B, wl.k
+    ws = mv.alloc_workspace(mv.MODE_DRAFT, B, 1, wl.H, wl.V, mv.DTYPE_BF16, dev())
+    for step in range(2):
+        case = Case(wl, W_store, W64, step, Wd)
+        drafts = torch.empty((B, k), dtype=torch.int32, device=dev())
+        for j in range(k):
+            col = torch.empty((B, 1), dtype=torch.int32, device=dev())
+            mv.spec_draft_sample(case.xd_d[:, j:j + 1].contiguous(), Wd, wl.T, wl.seed, step, j, col, ws)
+            drafts[:, j:j + 1] = col
+        got = drafts.cpu().numpy()
+        Q = oracle.softmax(oracle.lm_head_logits(case.Xd, W64), wl.T)
+        _, _, u_draft = oracle.verify_uniforms(wl.seed, step, B, k)
+        tok, lo, hi = oracle.inverse_cdf(Q.reshape(-1, wl.V), u_draft.reshape(-1))
+        near = (np.abs(u_draft.reshape(-1) - lo) <= 1e-5) | (np.abs(u_draft.reshape(-1) - hi) <= 1e-5)
+        assert not np.any((got.reshape(-1) != tok) & ~near)
+        klen = np.full(B, k, dtype=np.int32)
+        a, out, err = _call_ragged(case, "sample", drafts, None)
+        assert err == 0
+        _compare_ragged(case, "sample", a, out, got, klen)
