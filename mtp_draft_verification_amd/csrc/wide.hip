@@ -93,11 +93,13 @@ struct WideCfg {
     static constexpr int LDS = NSW * WSTAGE + NSX * XSTAGE;
     static_assert(NSW >= NSX && NSX >= 2 && LDS <= LDS_MAX, "rings");
     static_assert(LPW_W * RPI * (NT / 64) == BV && LPW_X * RPI * (NT / 64) == BM, "whole instructions");
-    // Loads issued after the later of X(kb) and W(kb), in issue order (each
-    // iteration i issues X(i + NSX - 1), then W(i + NSW - 1)).
-    static constexpr int WAIT = NSW > NSX ? LPW_W * (NSW - NSX) + (NSX - 2) * (LPW_W + LPW_X)
-                                          : (NSX - 2) * (LPW_W + LPW_X);
-    static_assert(NSW - NSX <= 1 && WAIT < 64, "wait count");
+    // The loop issues, in the middle of iteration i, X(i + NSX) then W(i + NSW)
+    // (the prologue does so for i = -NSW .. -1). WAIT: loads issued after the later
+    // of X(kb + 1) and W(kb + 1) when iteration kb waits for stage kb + 1; PRO_WAIT:
+    // loads issued after the later of X(0) and W(0) at the end of the prologue.
+    static constexpr int WAIT = NSW > NSX ? LPW_W + (NSX - 2) * (LPW_W + LPW_X) : (NSX - 2) * (LPW_W + LPW_X);
+    static constexpr int PRO_WAIT = NSW > NSX ? LPW_W + (NSX - 1) * (LPW_W + LPW_X) : (NSX - 1) * (LPW_W + LPW_X);
+    static_assert(NSW - NSX <= 1 && PRO_WAIT < 64, "wait counts");
 };
 
 // Workgroup barrier for the stage ring. __syncthreads() would also make every wave
@@ -105,8 +107,11 @@ struct WideCfg {
 // which drains the ring at every stage; the ring's own vmcnt wait already covers
 // the stage about to be read, so only the barrier itself is needed. The empty asm
 // statements keep the compiler from moving LDS accesses across it.
+// It also waits for this wave's LDS reads (lgkmcnt(0)), so that once every wave is
+// past it the buffers they read may be refilled.
 __device__ __forceinline__ void stage_barrier() {
     asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt at their maxima
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
@@ -215,10 +220,11 @@ __global__ __launch_bounds__(512, 1) void wide_kernel(LmHeadArgs p) {
             __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + i * 1024), 16, 0, 0);
         }
     };
-    // iteration i issues X(i + NSX - 1), then W(i + NSW - 1), each if it exists
-    auto issue_iter = [&](int i) {
-        if (i + NSX - 1 >= 0 && i + NSX - 1 < nk) issue_x(i + NSX - 1);
-        if (i + NSW - 1 >= 0 && i + NSW - 1 < nk) issue_w(i + NSW - 1);
+    // the middle of iteration i issues X(i + NSX), then W(i + NSW), each if it exists,
+    // into the buffers of stage i (read to registers by then)
+    auto issue_mid = [&](int i) {
+        if (i + NSX >= 0 && i + NSX < nk) issue_x(i + NSX);
+        if (i + NSW >= 0 && i + NSW < nk) issue_w(i + NSW);
     };
 
     // fragment read offsets: row (l & 15) of a 16-row block, chunk 4 s + l / 16 for
@@ -235,35 +241,53 @@ __global__ __launch_bounds__(512, 1) void wide_kernel(LmHeadArgs p) {
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) acc[fv][fm] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll
-    for (int i = -(NSW - 1); i < 0; ++i) issue_iter(i);
-
-    for (int kb = 0; kb < nk; ++kb) {
-        // this wave's loads of stage kb are done when only later ones remain; the
-        // last of those counted, W(kb + NSW - 2), exists iff kb + NSW - 2 < nk
-        if (kb + NSW - 2 < nk) wait_vm<Cfg::WAIT>();
-        else wait_vm<0>();
-        stage_barrier();  // every wave's stage kb landed; stage kb - 1 fully read
-        issue_iter(kb);   // into the buffers stage kb - 1 used
-
+    // The K-steps of stage kb: fragments of K-step 0 were read before the stage
+    // began, those of K-step 1 are read before K-step 0's MFMAs. In the middle of the
+    // stage every wave holds all of stage kb in registers, so after the barrier its
+    // buffers take the loads of later stages, and K-step 0 of stage kb + 1 is read
+    // before K-step 1's MFMAs: the MFMAs already issued cover the barrier, the load
+    // issue and the LDS latency.
+    auto read_frags = [&](int kb, int s, u32x4_t (&a)[4], u32x4_t (&b)[FM]) {
         const uint8_t* wbase = wring + (kb % NSW) * Cfg::WSTAGE + (vw * 64) * ROWB;
         const uint8_t* xbase = xring + (kb % NSX) * Cfg::XSTAGE + (mw * (BM / 2)) * ROWB;
+        const int fo = s == 0 ? frag_off0 : frag_off1;
 #pragma unroll
-        for (int s = 0; s < Cfg::KS; ++s) {
-            const int fo = s == 0 ? frag_off0 : frag_off1;
-            u32x4_t a[4], b[FM];
+        for (int fv = 0; fv < 4; ++fv) a[fv] = *(const u32x4_t*)(wbase + fv * 16 * ROWB + fo);
 #pragma unroll
-            for (int fv = 0; fv < 4; ++fv) a[fv] = *(const u32x4_t*)(wbase + fv * 16 * ROWB + fo);
+        for (int fm = 0; fm < FM; ++fm) b[fm] = *(const u32x4_t*)(xbase + fm * 16 * ROWB + fo);
+    };
+    auto mma = [&](const u32x4_t (&a)[4], const u32x4_t (&b)[FM]) {
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm) b[fm] = *(const u32x4_t*)(xbase + fm * 16 * ROWB + fo);
+        for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm)
+            for (int fv = 0; fv < 4; ++fv)
+                acc[fv][fm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[fv]),
+                                                                      __builtin_bit_cast(bf16x8_t, b[fm]),
+                                                                      acc[fv][fm], 0, 0, 0);
+    };
+    static_assert(Cfg::KS == 2, "two K-steps per stage");
+
 #pragma unroll
-                for (int fv = 0; fv < 4; ++fv)
-                    acc[fv][fm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[fv]),
-                                                                          __builtin_bit_cast(bf16x8_t, b[fm]),
-                                                                          acc[fv][fm], 0, 0, 0);
+    for (int i = -NSW; i < 0; ++i) issue_mid(i);
+    if (nk >= NSW) wait_vm<Cfg::PRO_WAIT>();
+    else wait_vm<0>();
+    stage_barrier();  // stage 0 landed in every wave
+    u32x4_t a0[4], b0[FM], a1[4], b1[FM];
+    read_frags(0, 0, a0, b0);
+
+    for (int kb = 0; kb < nk; ++kb) {
+        read_frags(kb, 1, a1, b1);
+        mma(a0, b0);
+        if (kb + 1 < nk) {
+            // this wave's loads of stage kb + 1 are done when only later ones remain;
+            // the last of those counted, W(kb + NSW - 1), exists iff kb + NSW - 1 < nk
+            if (kb + NSW - 1 < nk) wait_vm<Cfg::WAIT>();
+            else wait_vm<0>();
+            stage_barrier();  // stage kb + 1 landed everywhere; stage kb is in registers
+            issue_mid(kb);
+            read_frags(kb + 1, 0, a0, b0);
         }
+        mma(a1, b1);
     }
     __syncthreads();  // all stages read: the LDS is reused for the statistics
 
