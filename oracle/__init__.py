@@ -38,6 +38,7 @@ Layers:
                             greedy_verify_ragged, stochastic_verify_ragged
   random numbers          : philox.philox4x32_10, philox.verify_uniforms
   metrics                 : metrics.acceptance_metrics
+  MTP input fusion        : mtp_input.rms_norm, fused_input, mtp_input_fuse
 
 Every function is pinned by a `-m "not gpu"` test against something other than
 itself (exact rational enumeration, closed forms, library routines, an
@@ -62,6 +63,7 @@ from .verify import (
     verify_greedy_ragged_from_hidden,
     verify_sample_ragged_from_hidden,
 )
+from .mtp_input import rms_norm, fused_input, mtp_input_fuse
 from .philox import philox4x32_10, uniform24, verify_uniforms
 from .metrics import acceptance_metrics
 
@@ -71,5 +73,6 @@ __all__ = [
     "verify_greedy_from_hidden", "verify_sample_from_hidden", "draft_from_hidden",
     "greedy_verify_ragged", "stochastic_verify_ragged", "verify_greedy_ragged_from_hidden",
     "verify_sample_ragged_from_hidden",
+    "rms_norm", "fused_input", "mtp_input_fuse",
     "philox4x32_10", "uniform24", "verify_uniforms", "acceptance_metrics",
 ]
