@@ -76,6 +76,7 @@ typedef enum mtpv_mode { MTPV_MODE_GREEDY = 0, MTPV_MODE_SAMPLE = 1, MTPV_MODE_D
 /* Bits of the per-call device error word. */
 #define MTPV_DEVERR_DRAFT_RANGE 1 /* some draft id was outside [0, V); it was rejected */
 #define MTPV_DEVERR_DRAFT_LEN 2   /* some draft_len[b] was outside [0, k]; it was clamped */
+#define MTPV_DEVERR_TOKEN_RANGE 4 /* mtp_input_fuse: some token was outside [0, V); zero embedding used */
 
 /*
  * Optional exports for parity tests; pass NULL (or NULL members) in production.
@@ -220,6 +221,29 @@ MTPV_API int spec_verify_dual(const void* target_hidden, const void* draft_hidde
                        int32_t* accepted_len_sample, int32_t* out_tokens_sample,
                        void* workspace, size_t workspace_bytes,
                        const mtpv_debug* debug, void* stream);
+
+/*
+ * Input fusion of the MTP module in front of the drafter ("The Tiny Draft Model
+ * Hidden Inside Qwen", section "One step deeper than the main model": the module
+ * takes the main model's final hidden state and the embedding of the chosen token,
+ * normalizes both, concatenates them and projects back to the hidden width with
+ * mtp.fc; the embedding table is the main model's, section "What vLLM and SGLang do
+ * with the weights"). The page's formula did not survive; the reading is
+ *   n(v)   = v / sqrt(mean(v^2) + eps) * g                 (RMS normalization)
+ *   x[b]   = [ n(embed[tokens[b]]; norm_emb) | n(hidden[b]; norm_hidden) ]   (2H)
+ *   out[b] = x[b] . W_fc^T                                  (no bias)
+ * tokens [B] int32; embed [V, H], hidden [B, H], norm_emb [H], norm_hidden [H],
+ * W_fc [H, 2H] (rows = outputs): bf16, row-major, 16-byte aligned, H % 8 == 0;
+ * out [B, H] fp32. The fused input is rounded to bf16 (the projection's input
+ * type) after fp32 normalization; the product accumulates in fp32. A token outside
+ * [0, V) contributes a zero embedding half and sets MTPV_DEVERR_TOKEN_RANGE.
+ * eps >= 0 and finite. Workspace: mtpv_fuse_workspace_bytes(B, H).
+ */
+MTPV_API size_t mtpv_fuse_workspace_bytes(int B, int H);
+MTPV_API int mtp_input_fuse(const int32_t* tokens, const void* embed, const void* hidden,
+                       const void* norm_emb, const void* norm_hidden, const void* W_fc,
+                       int B, int H, int V, double eps, float* out,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Drafter-side sampling through the same shared head: for each request b and

@@ -13,6 +13,8 @@ Calls (names as in the C ABI):
   spec_verify_greedy_ragged / spec_verify_sample_ragged(..., draft_len[B], ...)  per-request draft counts
   spec_verify_dual(target_hidden, draft_hidden, W, drafts, draft_len, temperature, seed, offset,
                    accepted_len_greedy, out_tokens_greedy, accepted_len_sample, out_tokens_sample, workspace)
+  mtp_input_fuse(tokens[B], embed[V,H], hidden[B,H], norm_emb[H], norm_hidden[H], W_fc[H,2H], eps, out[B,H],
+                 workspace)
 """
 import ctypes
 import os
@@ -24,6 +26,7 @@ MODE_GREEDY, MODE_SAMPLE, MODE_DRAFT = 0, 1, 2
 DTYPE_BF16, DTYPE_F32 = 0, 1
 DEVERR_DRAFT_RANGE = 1
 DEVERR_DRAFT_LEN = 2
+DEVERR_TOKEN_RANGE = 4
 
 STATUS = {0: "MTPV_OK", -1: "MTPV_EINVAL", -2: "MTPV_EALIGN", -3: "MTPV_EWORKSPACE", -4: "MTPV_EDTYPE",
           -5: "MTPV_ENULL", -6: "MTPV_ELAUNCH", -7: "MTPV_EDEVICE"}
@@ -60,6 +63,8 @@ _SIGNATURES = {
                                        _vp, _sz, _vp, _vp]),
     "spec_verify_dual": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _d, _u64, _u64, _vp, _vp, _vp, _vp,
                               _vp, _sz, _vp, _vp]),
+    "mtpv_fuse_workspace_bytes": (_sz, [_i, _i]),
+    "mtp_input_fuse": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _d, _vp, _vp, _sz, _vp]),
     "mtpv_device_error": (_i, [_vp, ctypes.POINTER(ctypes.c_int32), _vp]),
     "mtpv_timing_enable": (_i, [_i]),
     "mtpv_timing_read": (_i, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), _i]),
@@ -222,6 +227,27 @@ def spec_verify_dual(target_hidden, draft_hidden, W, drafts, draft_len, temperat
                                 _ptr(accepted_len_sample), _ptr(out_tokens_sample), _ptr(workspace),
                                 workspace.numel(), _dbg(debug), _stream(stream))
     _check(st, "spec_verify_dual")
+
+
+def alloc_fuse_workspace(B, H, device):
+    import torch
+    n = lib().mtpv_fuse_workspace_bytes(B, H)
+    if n == 0:
+        raise MtpvError(-1, "mtpv_fuse_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def mtp_input_fuse(tokens, embed, hidden, norm_emb, norm_hidden, W_fc, eps, out, workspace, stream=None):
+    """MTP input fusion: tokens [B] int32, embed [V,H], hidden [B,H], norms [H], W_fc [H,2H] (bf16)
+    -> out [B,H] fp32 = [rms(embed[tok]) | rms(hidden)] @ W_fc^T."""
+    B, H = hidden.shape
+    V = embed.shape[0]
+    for n, t in (("tokens", tokens), ("embed", embed), ("hidden", hidden), ("norm_emb", norm_emb),
+                 ("norm_hidden", norm_hidden), ("W_fc", W_fc), ("out", out), ("workspace", workspace)):
+        _contig(n, t)
+    st = lib().mtp_input_fuse(_ptr(tokens), _ptr(embed), _ptr(hidden), _ptr(norm_emb), _ptr(norm_hidden), _ptr(W_fc),
+                              B, H, V, float(eps), _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "mtp_input_fuse")
 
 
 def spec_draft_sample(draft_hidden, W, temperature, seed, offset, depth0, draft_tokens, workspace, debug=None,

@@ -240,32 +240,15 @@ int check_debug(const Plan& plan, const mtpv_debug* dbg) {
     return MTPV_OK;
 }
 
-// One call: the LM-head launch, the decision pass (two passes for the dual call,
-// greedy first, into alen_g / out_g), and the sampling passes.
-int run(const Plan& plan, const void* xt, const void* xd, const void* w, const int32_t* drafts,
-        const int32_t* draft_len, double temperature, uint64_t seed, uint64_t offset, int depth0,
-        int32_t* alen, int32_t* out, void* ws, const mtpv_debug* dbg, hipStream_t stream,
-        int32_t* alen_g = nullptr, int32_t* out_g = nullptr) {
-    uint8_t* base = static_cast<uint8_t*>(ws);
-    int32_t* err = reinterpret_cast<int32_t*>(base + plan.off_err);
-    Partial* partials = reinterpret_cast<Partial*>(base + plan.off_partials);
-    float* dlogit = reinterpret_cast<float*>(base + plan.off_dlogit);
-    RowStat* rowstat = reinterpret_cast<RowStat*>(base + plan.off_rowstat);
-    Job* jobs = reinterpret_cast<Job*>(base + plan.off_jobs);
-    double* zpart = reinterpret_cast<double*>(base + plan.off_zpart);
-    double* tsum = reinterpret_cast<double*>(base + plan.off_tsum);
-    float* spill = nullptr;
-    if (plan.mode != MTPV_MODE_GREEDY) spill = reinterpret_cast<float*>(base + plan.off_spill);
-    if (dbg && dbg->logits) spill = dbg->logits;
-
-    const double T = plan.mode == MTPV_MODE_GREEDY ? 1.0 : temperature;
-    const float c2f = (float)(kLog2e / T);
-
+// The LM-head kernel of `plan` on rows xt (then xd) against w, with the timing
+// events around it when enabled.
+int launch_head(const Plan& plan, const void* xt, const void* xd, const void* w, const int32_t* drafts, float c2f,
+                Partial* partials, float* dlogit, float* spill, int32_t* err, hipStream_t stream) {
     LmHeadArgs la;
     la.xt = static_cast<const uint8_t*>(xt);
     la.xd = static_cast<const uint8_t*>(xd);
     la.w = static_cast<const uint8_t*>(w);
-    la.drafts = plan.mode == MTPV_MODE_DRAFT ? nullptr : drafts;
+    la.drafts = drafts;
     la.Mt = plan.Mt;
     la.Meff = plan.Meff;
     la.H = plan.H;
@@ -292,6 +275,33 @@ int run(const Plan& plan, const void* xt, const void* xd, const void* w, const i
                                                    : launch_lmhead(plan, la, stream);
     if (le != hipSuccess) return MTPV_ELAUNCH;
     if (ev && hipEventRecord(ev->second, stream) != hipSuccess) return MTPV_EDEVICE;
+    return MTPV_OK;
+}
+
+// One call: the LM-head launch, the decision pass (two passes for the dual call,
+// greedy first, into alen_g / out_g), and the sampling passes.
+int run(const Plan& plan, const void* xt, const void* xd, const void* w, const int32_t* drafts,
+        const int32_t* draft_len, double temperature, uint64_t seed, uint64_t offset, int depth0,
+        int32_t* alen, int32_t* out, void* ws, const mtpv_debug* dbg, hipStream_t stream,
+        int32_t* alen_g = nullptr, int32_t* out_g = nullptr) {
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    int32_t* err = reinterpret_cast<int32_t*>(base + plan.off_err);
+    Partial* partials = reinterpret_cast<Partial*>(base + plan.off_partials);
+    float* dlogit = reinterpret_cast<float*>(base + plan.off_dlogit);
+    RowStat* rowstat = reinterpret_cast<RowStat*>(base + plan.off_rowstat);
+    Job* jobs = reinterpret_cast<Job*>(base + plan.off_jobs);
+    double* zpart = reinterpret_cast<double*>(base + plan.off_zpart);
+    double* tsum = reinterpret_cast<double*>(base + plan.off_tsum);
+    float* spill = nullptr;
+    if (plan.mode != MTPV_MODE_GREEDY) spill = reinterpret_cast<float*>(base + plan.off_spill);
+    if (dbg && dbg->logits) spill = dbg->logits;
+
+    const double T = plan.mode == MTPV_MODE_GREEDY ? 1.0 : temperature;
+    const float c2f = (float)(kLog2e / T);
+
+    const int hs = launch_head(plan, xt, xd, w, plan.mode == MTPV_MODE_DRAFT ? nullptr : drafts, c2f, partials,
+                               dlogit, spill, err, stream);
+    if (hs != MTPV_OK) return hs;
 
     DecideArgs da;
     da.partials = partials;
@@ -466,6 +476,60 @@ int spec_verify_dual(const void* target_hidden, const void* draft_hidden, const 
     return run(p, target_hidden, draft_hidden, W_lm, draft_tokens, draft_len, temperature, seed, offset, 0,
                accepted_len_sample, out_tokens_sample, workspace, debug, static_cast<hipStream_t>(stream),
                accepted_len_greedy, out_tokens_greedy);
+}
+
+// Workspace of mtp_input_fuse: the projection's LM-head workspace (its error word
+// first), then the fused rows [B, 2H] bf16.
+static int fuse_plan(int B, int H, Plan* p, size_t* x_off, size_t* total) {
+    if (H < 8 || H > (1 << 19)) return MTPV_EINVAL;
+    const int st = make_plan(MTPV_MODE_GREEDY, B, 0, 2 * H, H, MTPV_BF16, p);
+    if (st != MTPV_OK) return st;
+    *x_off = align_up(p->total, 256);
+    *total = *x_off + align_up((size_t)B * 2 * H * 2, 256);
+    return MTPV_OK;
+}
+
+size_t mtpv_fuse_workspace_bytes(int B, int H) {
+    Plan p;
+    size_t x_off, total;
+    return fuse_plan(B, H, &p, &x_off, &total) == MTPV_OK ? total : 0;
+}
+
+int mtp_input_fuse(const int32_t* tokens, const void* embed, const void* hidden, const void* norm_emb,
+                   const void* norm_hidden, const void* W_fc, int B, int H, int V, double eps, float* out,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+    Plan p;
+    size_t x_off, total;
+    if (B < 1 || V < 1 || V > (1 << 26) || !(std::isfinite(eps) && eps >= 0.0)) return MTPV_EINVAL;
+    int st = fuse_plan(B, H, &p, &x_off, &total);
+    if (st != MTPV_OK) return st;
+    if (H % 8 != 0) return MTPV_EALIGN;
+    if (!tokens || !embed || !hidden || !norm_emb || !norm_hidden || !W_fc || !out) return MTPV_ENULL;
+    if (!aligned(tokens, 4) || !aligned(embed, 16) || !aligned(hidden, 16) || !aligned(norm_emb, 16) ||
+        !aligned(norm_hidden, 16) || !aligned(W_fc, 16) || !aligned(out, 16))
+        return MTPV_EALIGN;
+    if (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < total) return MTPV_EWORKSPACE;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* base = static_cast<uint8_t*>(workspace);
+    FuseArgs fa;
+    fa.tokens = tokens;
+    fa.embed = static_cast<const uint8_t*>(embed);
+    fa.hidden = static_cast<const uint8_t*>(hidden);
+    fa.g_e = static_cast<const uint8_t*>(norm_emb);
+    fa.g_h = static_cast<const uint8_t*>(norm_hidden);
+    fa.x = base + x_off;
+    fa.err = reinterpret_cast<int32_t*>(base + p.off_err);
+    fa.B = B;
+    fa.H = H;
+    fa.V = V;
+    fa.eps = (float)eps;
+    if (launch_fuse(fa, s) != hipSuccess) return MTPV_ELAUNCH;
+    // the projection: fused rows in the place of hidden states, W_fc in the place of
+    // the head, the fp32 result through the logit output; the error word is the
+    // fusion kernel's
+    return launch_head(p, base + x_off, nullptr, W_fc, nullptr, (float)kLog2e,
+                       reinterpret_cast<Partial*>(base + p.off_partials), reinterpret_cast<float*>(base + p.off_dlogit),
+                       out, nullptr, s);
 }
 
 int spec_draft_sample(const void* draft_hidden, const void* W_lm, int B, int kd, int depth0, int H, int V,

@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256) void lmhead_kernel(LmHeadArgs p) {
         vb = (slot / p.MC) * 8 + (L & 7);
         if (vb >= p.S) return;  // uniform over the workgroup
     }
-    if (vb == 0 && mc == 0 && tid == 0) *p.err = 0;
+    if (vb == 0 && mc == 0 && tid == 0 && p.err != nullptr) *p.err = 0;
 
     const int m0 = mc * 16 * NT;
     const int mrows = min(16 * NT, p.Meff - m0);

@@ -77,7 +77,7 @@ struct LmHeadArgs {
     Partial* partials;      // [Meff, S]
     float* dlogit;          // [Meff]
     float* spill;           // [Meff, V] or NULL
-    int32_t* err;           // cleared by the first workgroup
+    int32_t* err;           // cleared by the first workgroup (NULL: left alone)
     int tiles;              // skinny kernel: 4-row tiles per wave
     int rotate;             // skinny / wide kernels: rotation of the K order per wave / workgroup
 };
@@ -132,5 +132,19 @@ struct ProbsArgs {
 hipError_t launch_probs(const ProbsArgs& args, hipStream_t stream);
 
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
+struct FuseArgs {
+    const int32_t* tokens;  // [B]
+    const uint8_t* embed;   // [V, H] bf16
+    const uint8_t* hidden;  // [B, H] bf16
+    const uint8_t* g_e;     // [H] bf16
+    const uint8_t* g_h;     // [H] bf16
+    uint8_t* x;             // [B, 2H] bf16 (output)
+    int32_t* err;           // device error word (written by workgroup 0)
+    int B, H, V;
+    float eps;
+};
+
+hipError_t launch_fuse(const FuseArgs& args, hipStream_t stream);
 
 }  // namespace mtpv

@@ -113,7 +113,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(LmHeadArgs p) {
     const int mrows = p.Meff;  // all positions fit one workgroup here
     const int pitch = nsteps * KS * ES + 64;
 
-    if (vb == 0 && tid == 0) *p.err = 0;
+    if (vb == 0 && tid == 0 && p.err != nullptr) *p.err = 0;
 
     // Address of this lane's 16 bytes for the next step to load; steps advance
     // through K of the current tile, then on to the next tile. Past the last step

@@ -158,7 +158,7 @@ __global__ __launch_bounds__(512, 1) void wide_kernel(LmHeadArgs p) {
         vt = (idx / p.MC) * 8 + (g & 7);
         if (vt >= S) return;  // uniform over the workgroup
     }
-    if (vt == 0 && mt == 0 && tid == 0) *p.err = 0;
+    if (vt == 0 && mt == 0 && tid == 0 && p.err != nullptr) *p.err = 0;
 
     // vocabulary rows [v0, v1) of this tile: the 16-row groups of V split evenly over
     // the S tiles (edges on 16-row boundaries keep the fp32 spill's vector stores

@@ -139,3 +139,18 @@ def hidden(wl: Workload, step: int):
     if wl.dtype == "bf16":
         return round_to_bf16(h), round_to_bf16(hd)
     return h, hd
+
+
+def fuse_inputs(H, V, B, cid=300, step=0, embed=True):
+    """Seeded inputs of the MTP input fusion (bf16 bits unless noted):
+    stream 4: embedding table E [V, H] ~ N(0, 1) * 0.02 (skipped when embed=False;
+              the benchmark passes the head W in its place);
+    stream 5: hidden h [B, H] ~ N(0, 1); stream 6: the two norm weights [H] ~ N(1, 0.1);
+    stream 7: W_fc [H, 2H] ~ N(0, 1) * 0.02; stream 8: tokens [B] int32 uniform in [0, V).
+    """
+    E = round_to_bf16(_rng(cid, 4, 0).standard_normal((V, H), dtype=np.float32) * np.float32(0.02)) if embed else None
+    h = round_to_bf16(_rng(cid, 5, step).standard_normal((B, H), dtype=np.float32))
+    g = _rng(cid, 6, 0).normal(1.0, 0.1, size=(2, H)).astype(np.float32)
+    W_fc = round_to_bf16(_rng(cid, 7, 0).standard_normal((H, 2 * H), dtype=np.float32) * np.float32(0.02))
+    tokens = _rng(cid, 8, step).integers(0, V, size=B).astype(np.int32)
+    return tokens, E, h, round_to_bf16(g[0]), round_to_bf16(g[1]), W_fc

@@ -143,3 +143,31 @@ def test_ragged_and_dual_calls_validate_on_the_host():
                               vp(A), vp(A), vp(WS), 1 << 30, None, None) == -5
     assert L.spec_verify_dual(vp(A), vp(A), vp(A), vp(A), None, 2, 3, 256, 1000, 0, 1.0, 0, 0, vp(A), vp(A),
                               vp(A), vp(A), vp(WS), ws_small, None, None) == -3
+
+
+def test_fuse_call_validates_on_the_host():
+    """mtp_input_fuse: workspace sizing and every host-side error, without a GPU."""
+    L = mv.lib()
+    vp = ctypes.c_void_p
+    assert L.mtpv_fuse_workspace_bytes(4, 5120) > 4 * 2 * 5120 * 2
+    assert L.mtpv_fuse_workspace_bytes(0, 5120) == 0
+    assert L.mtpv_fuse_workspace_bytes(4, 4) == 0
+    ok = dict(tokens=vp(A), embed=vp(A), hidden=vp(A), ne=vp(A), nh=vp(A), W=vp(A), B=4, H=256, V=1000, eps=1e-6,
+              out=vp(A), ws=vp(WS), wsb=1 << 30)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.mtp_input_fuse(a["tokens"], a["embed"], a["hidden"], a["ne"], a["nh"], a["W"], a["B"], a["H"],
+                                a["V"], a["eps"], a["out"], a["ws"], a["wsb"], None)
+    assert call(B=0) == -1
+    assert call(V=0) == -1
+    assert call(eps=-1.0) == -1
+    assert call(eps=float("nan")) == -1
+    assert call(H=260) == -2
+    assert call(embed=None) == -5
+    assert call(W=None) == -5
+    assert call(out=vp(A + 4)) == -2
+    assert call(tokens=vp(A + 2)) == -2
+    assert call(hidden=vp(A + 8)) == -2
+    assert call(wsb=1024) == -3
+    assert call(ws=vp(WS + 16)) == -3
