@@ -1,6 +1,8 @@
 """Benchmark of the vocab-side verify step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--mode greedy|sample]
+    python bench.py --op fuse --workload 3     (MTP input fusion at that width and batch)
+    python bench.py --sweep                    (greedy verify time against M_eff, one line per M)
 
 One step = one verify call (the whole hot path: LM-head stream + fused softmax/argmax
 epilogue, cross-block combine, acceptance decisions and prefix scan, and in sample
@@ -40,7 +42,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-LMHEAD_SOURCES = ("lmhead.hip", "skinny.hip", "wide.hip", "mtpv_internal.h", "api.hip")
+LMHEAD_SOURCES = ("lmhead.hip", "skinny.hip", "wide.hip", "mtpv_internal.h", "plan.hip")
 
 
 def lmhead_source_hash():
@@ -108,6 +110,94 @@ def cpu_baseline(wl, mode, W_store, budget_s):
                       f"{t_total:.1f} s of oracle time; accepted tokens/s {accepted / t_total:.3g}"}
 
 
+def _events_time(fn, steps, warmup):
+    """Wall time per call (host clock around synchronised loops) and the library's
+    LM-head kernel time per call (HIP events on the call's stream)."""
+    import torch
+    import mtp_draft_verification_amd as mv
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    mv.timing_enable(True)
+    mv.timing_read(reset=True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    kern_ms, n = mv.timing_read(reset=True)
+    mv.timing_enable(False)
+    return wall, kern_ms / 1e3 / max(n, 1)
+
+
+def sweep(args):
+    """Greedy verify against the number of head rows, H = 5120, V = 151936 (the
+    batched / depth-5 head): flat while HBM-bound, rising past the ridge."""
+    import torch
+    import mtp_draft_verification_amd as mv
+    dev = torch.device("cuda:0")
+    H, V = 5120, 151936
+    wl0 = synth.custom(H=H, V=V, B=1, k=3, cid=3, name="sweep_head")
+    log(f"sweep: generating W [{V}, {H}] bf16")
+    W = torch.from_numpy(synth.weights(wl0).view(np.int16)).view(torch.bfloat16).to(dev)
+    for M in (1, 4, 16, 64, 128, 224, 384, 704, 1024, 1792):
+        k = 0 if M == 1 else 3
+        B = M // (k + 1)
+        wl = synth.custom(H=H, V=V, B=B, k=k, cid=400 + M)
+        xt, _ = synth.hidden(wl, 0)
+        xt_d = torch.from_numpy(np.ascontiguousarray(xt).view(np.int16)).view(torch.bfloat16).to(dev)
+        drafts = torch.zeros((B, k), dtype=torch.int32, device=dev)
+        alen = torch.zeros(B, dtype=torch.int32, device=dev)
+        out = torch.zeros((B, k + 1), dtype=torch.int32, device=dev)
+        ws = mv.alloc_workspace(mv.MODE_GREEDY, B, k, H, V, mv.DTYPE_BF16, dev)
+        wall, kern = _events_time(lambda: mv.spec_verify_greedy(xt_d, W, drafts, alen, out, ws), args.steps, args.warmup)
+        alg_bytes = V * H * 2 + M * H * 2
+        print(json.dumps({"sweep": "greedy_verify_H5120_V151936", "M_eff": M, "B": B, "k": k,
+                          "ms_per_call": round(wall * 1e3, 4), "kernel_us": round(kern * 1e6, 2),
+                          "hbm_frac": round(alg_bytes / kern / 8e12, 4),
+                          "mfma_frac": round(2.0 * M * H * V / kern / 2.5e15, 4)}), flush=True)
+
+
+def bench_fuse(args, wl):
+    """MTP input fusion at the workload's width and batch: tokens gathered from the head
+    W (standing in for the shared embedding table, same shape), fc [H, 2H]."""
+    import torch
+    import mtp_draft_verification_amd as mv
+    dev = torch.device("cuda:0")
+    H, V, B = wl.H, wl.V, wl.B
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    log(f"fuse: H={H} V={V} B={B}; generating the table [{V}, {H}] and fc [{H}, {2 * H}]")
+    E = bf(synth.weights(wl))
+    pool = []
+    for s in range(max(1, min(args.pool, 8))):
+        tokens, _, h, ge, gh, Wfc = synth.fuse_inputs(H, V, B, step=s, embed=False)
+        pool.append((torch.from_numpy(tokens).to(dev), bf(h)))
+    ge_d, gh_d, Wfc_d = bf(ge), bf(gh), bf(Wfc)
+    out = torch.empty((B, H), dtype=torch.float32, device=dev)
+    ws = mv.alloc_fuse_workspace(B, H, dev)
+    it = [0]
+
+    def call():
+        tok, h = pool[it[0] % len(pool)]
+        it[0] += 1
+        mv.mtp_input_fuse(tok, E, h, ge_d, gh_d, Wfc_d, 1e-6, out, ws)
+
+    wall, kern = _events_time(call, args.steps, args.warmup)
+    alg = H * 2 * H * 2 + B * 2 * H * 2          # fc weights once + the fused rows
+    line = {"metric": "MTP input fusion rows/s (RMS-normalized embedding | hidden, fc 2H -> H)",
+            "value": round(B / wall, 1), "unit": "rows/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"mtp_input_fuse_H{H}_B{B}", "H": H, "B": B, "V": V},
+            "roofline": {"bound": "hbm", "achieved": round(alg / kern / 1e9, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(alg / kern / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                         "kernel_us": round(kern * 1e6, 2), "algorithmic_bytes_per_launch": alg}}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,6 +211,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run the library's plain copy kernel on this many MiB (counter calibration)")
+    ap.add_argument("--op", choices=["verify", "fuse"], default="verify",
+                    help="verify (default) or the MTP input fusion at the workload's H and B")
+    ap.add_argument("--sweep", action="store_true",
+                    help="greedy verify time against M_eff at H=5120, V=151936 (one JSON line per M)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -132,7 +226,11 @@ def main():
     import torch
     import mtp_draft_verification_amd as mv
 
+    if args.sweep:
+        return sweep(args)
     wl = synth.WORKLOADS[args.workload]
+    if args.op == "fuse":
+        return bench_fuse(args, wl)
     mode = args.mode or wl.modes[0]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

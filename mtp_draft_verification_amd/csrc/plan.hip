@@ -1,0 +1,162 @@
+// Launch plan of a verify call: which LM-head kernel, its tiling and grid, the
+// sampling-pass chunking, and the workspace layout. Host code only; everything that
+// decides how the LM-head kernels are launched lives here.
+#include "mtpv.h"
+#include "mtpv_internal.h"
+
+#include <algorithm>
+#include <cstring>
+
+namespace mtpv {
+
+namespace {
+
+constexpr int kMaxK = 64;
+constexpr int kLdsBudget = 64 * 1024;   // staging budget per workgroup (two workgroups fit per CU)
+constexpr size_t kLdsPerCU = 160 * 1024; // LDS of one gfx950 compute unit
+constexpr int kCUs = 256;                // compute units of one MI355X
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int shape_status(int mode, int B, int k, int H, int V, int dtype) {
+    if (dtype != MTPV_BF16 && dtype != MTPV_F32) return MTPV_EDTYPE;
+    if (mode < MTPV_MODE_GREEDY || mode > MTPV_MODE_DRAFT) return MTPV_EINVAL;
+    if (B < 1 || B > (1 << 20) || k < 0 || k > kMaxK || H < 8 || H > (1 << 20) || V < 1 || V > (1 << 26))
+        return MTPV_EINVAL;
+    if (mode == MTPV_MODE_DRAFT && k < 1) return MTPV_EINVAL;
+    if (H % 8 != 0) return MTPV_EALIGN;
+    const long long meff = (long long)B * (k + 1) + (mode == MTPV_MODE_SAMPLE ? (long long)B * k : 0);
+    if (meff > (1 << 22)) return MTPV_EINVAL;
+    // sampling jobs and debug rows index the second grid dimension (at most 65535)
+    if (mode == MTPV_MODE_DRAFT && (long long)B * k > 65535) return MTPV_EINVAL;
+    if (meff > 65535) return MTPV_EINVAL;
+    return MTPV_OK;
+}
+
+}  // namespace
+
+int make_plan(int mode, int B, int k, int H, int V, int dtype, Plan* pl) {
+    const int st = shape_status(mode, B, k, H, V, dtype);
+    if (st != MTPV_OK) return st;
+    Plan p;
+    std::memset(&p, 0, sizeof(p));
+    p.mode = mode;
+    p.B = B;
+    p.k = k;
+    p.H = H;
+    p.V = V;
+    p.dtype = dtype;
+    p.es = dtype == MTPV_BF16 ? 2 : 4;
+    if (mode == MTPV_MODE_DRAFT) {
+        p.Mt = 0;
+        p.Meff = B * k;
+    } else {
+        p.Mt = B * (k + 1);
+        p.Meff = p.Mt + (mode == MTPV_MODE_SAMPLE ? B * k : 0);
+    }
+    const int epv = 16 / p.es;
+    // Few positions (<= 16) whose hidden states fit in LDS: the streaming kernel
+    // with 4-row tiles (p.tiles tiles per wave, 16 * tiles rows per workgroup).
+    {
+        const int ks = 16 * epv;
+        const int nsteps = (H + ks - 1) / ks;
+        const size_t pitch = (size_t)nsteps * ks * p.es + 64;
+        const size_t x_lds = (size_t)p.Meff * pitch;
+        if (p.Meff <= 16 && x_lds <= (size_t)kLdsBudget) {
+            // One resident round: kCUs compute units times the workgroups their LDS
+            // holds, but no more workgroups than there are 16-row groups of tiles.
+            p.kind = KIND_SKINNY;
+            const int per_cu = (int)std::min<size_t>(8, kLdsPerCU / std::max<size_t>(x_lds, 1024));
+            const int tiles = (V + 3) / 4;
+            p.grid = std::max(1, std::min(kCUs * std::max(per_cu, 1), (tiles + 3) / 4));
+            p.tiles = (tiles + 4 * p.grid - 1) / (4 * p.grid);
+            p.vblock = 0;
+            p.S = p.grid;
+            p.MC = 1;
+            p.lds = std::max(x_lds, (size_t)4 * 16 * 16);
+            p.va = p.nt = 0;
+            p.kc = H;
+        }
+    }
+    if (p.kind != KIND_SKINNY && p.es == 2) {
+        // Many positions, bf16: LDS-tiled matrix product, one workgroup per tile of at
+        // most 256 vocabulary rows by 128 or 256 positions (whichever pads fewer
+        // rows; 256 on a tie, so W is re-read from L2 fewer times), the position
+        // chunks of one vocabulary tile on one XCD. With few tiles the vocabulary is
+        // cut into more, smaller tiles so that every compute unit gets the same
+        // number (at least 16 rows per tile).
+        p.kind = KIND_WIDE;
+        const int pad128 = (p.Meff + 127) / 128 * 128;
+        const int pad256 = (p.Meff + 255) / 256 * 256;
+        const int bm = pad256 <= pad128 ? 256 : 128;
+        p.nt = bm;
+        p.MC = (p.Meff + bm - 1) / bm;
+        p.va = 0;
+        const long long s0 = (V + wide_rows() - 1) / wide_rows();
+        long long S = s0;
+        if (s0 * p.MC < 4LL * kCUs) {
+            const long long rounds = (s0 * p.MC + kCUs - 1) / kCUs;
+            S = std::max(s0, (rounds * kCUs + p.MC - 1) / p.MC);
+            S = std::min(S, std::max(s0, (long long)(V + 15) / 16));
+        }
+        p.S = (int)S;
+        p.grid = p.MC == 1 ? p.S : ((p.S + 7) / 8) * 8 * p.MC;
+        p.kc = 64;
+        p.lds = wide_lds_bytes(bm);
+        p.vblock = 0;
+    }
+    if (p.kind == KIND_TILE) {
+        // LM-head tile: positions in chunks of 16*nt, 16*va vocab rows per wave.
+        const int need = (p.Meff + 15) / 16;
+        if (p.es == 2) {
+            p.nt = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
+            p.va = p.nt == 1 ? 1 : 2;
+        } else {
+            p.va = 1;
+            p.nt = need <= 1 ? 1 : 2;
+        }
+        p.vblock = 64 * p.va;
+        p.S = (V + p.vblock - 1) / p.vblock;
+        p.MC = (p.Meff + 16 * p.nt - 1) / (16 * p.nt);
+        const int kstep = 4 * epv;
+        const int rows = std::min(16 * p.nt, p.Meff);
+        const int h_pad = (H + kstep - 1) / kstep * kstep;
+        int kc = ((kLdsBudget / rows - 16) / p.es) / kstep * kstep;
+        if (kc < kstep) kc = kstep;
+        p.kc = std::min(kc, h_pad);
+        const size_t stage = (size_t)rows * (p.kc * p.es + 16);
+        const size_t red = (size_t)4 * 16 * p.nt * sizeof(Partial);
+        p.lds = std::max(stage, red);
+        p.grid = p.MC == 1 ? p.S : ((p.S + 7) / 8) * 8 * p.MC;
+    }
+    // sampling jobs
+    p.ntiles = (V + 63) / 64;
+    p.NJ = mode == MTPV_MODE_GREEDY ? 0 : mode == MTPV_MODE_SAMPLE ? B : B * k;
+    if (p.NJ > 0) {
+        int c = (1024 + p.NJ - 1) / p.NJ;
+        c = std::max(1, std::min(c, 64));
+        p.C = std::min(c, p.ntiles);
+    }
+    // workspace layout
+    size_t off = 0;
+    p.off_err = off;
+    off = align_up(off + 4, 256);
+    p.off_partials = off;
+    off = align_up(off + (size_t)p.Meff * p.S * sizeof(Partial), 256);
+    p.off_dlogit = off;
+    off = align_up(off + (size_t)p.Meff * sizeof(float), 256);
+    p.off_rowstat = off;
+    off = align_up(off + (size_t)p.Meff * sizeof(RowStat), 256);
+    p.off_jobs = off;
+    off = align_up(off + (size_t)p.NJ * sizeof(Job), 256);
+    p.off_zpart = off;
+    off = align_up(off + (size_t)p.NJ * p.C * 2 * sizeof(double), 256);
+    p.off_tsum = off;
+    off = align_up(off + (size_t)p.NJ * p.ntiles * sizeof(double), 256);
+    p.off_spill = off;
+    if (mode != MTPV_MODE_GREEDY) off = align_up(off + (size_t)p.Meff * V * sizeof(float), 256);
+    p.total = off;
+    *pl = p;
+    return MTPV_OK;
+}
+
+}  // namespace mtpv
