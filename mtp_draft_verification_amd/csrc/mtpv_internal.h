@@ -46,7 +46,7 @@ struct Plan {
     int es;          // element size (2 for bf16, 4 for fp32)
     int Mt, Meff;    // target rows, all rows the head sees
     int va, nt;      // tile kernel: 16*va vocab rows per wave, 16*nt positions per chunk;
-                     // wide kernel: nt = positions per tile (128 or 256)
+                     // wide kernel: nt = positions per tile (64, 128 or 256)
     int vblock;      // vocab rows per workgroup (64 * va)
     int S;           // vocab blocks (wide kernel: tiles, V split evenly, at most 256 rows each)
     int MC;          // M chunks
@@ -85,7 +85,7 @@ struct LmHeadArgs {
 hipError_t launch_lmhead(const Plan& plan, const LmHeadArgs& args, hipStream_t stream);
 hipError_t launch_skinny(const Plan& plan, const LmHeadArgs& args, hipStream_t stream);
 hipError_t launch_wide(const Plan& plan, const LmHeadArgs& args, hipStream_t stream);
-size_t wide_lds_bytes(int bm);  // dynamic LDS of the wide kernel for bm (128 or 256) positions per tile
+size_t wide_lds_bytes(int bm);  // dynamic LDS of the wide kernel for bm (64, 128 or 256) positions per tile
 int wide_rows();                // most vocabulary rows per wide-kernel tile
 
 struct DecideArgs {

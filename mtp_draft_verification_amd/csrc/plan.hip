@@ -79,15 +79,16 @@ int make_plan(int mode, int B, int k, int H, int V, int dtype, Plan* pl) {
     }
     if (p.kind != KIND_SKINNY && p.es == 2) {
         // Many positions, bf16: LDS-tiled matrix product, one workgroup per tile of at
-        // most 256 vocabulary rows by 128 or 256 positions (whichever pads fewer
+        // most 256 vocabulary rows by 64, 128 or 256 positions (whichever pads fewer
         // rows; 256 on a tie, so W is re-read from L2 fewer times), the position
         // chunks of one vocabulary tile on one XCD. With few tiles the vocabulary is
         // cut into more, smaller tiles so that every compute unit gets the same
         // number (at least 16 rows per tile).
         p.kind = KIND_WIDE;
+        const int pad64 = (p.Meff + 63) / 64 * 64;
         const int pad128 = (p.Meff + 127) / 128 * 128;
         const int pad256 = (p.Meff + 255) / 256 * 256;
-        const int bm = pad256 <= pad128 ? 256 : 128;
+        const int bm = pad256 <= pad128 ? 256 : pad128 <= pad64 ? 128 : 64;
         p.nt = bm;
         p.MC = (p.Meff + bm - 1) / bm;
         p.va = 0;

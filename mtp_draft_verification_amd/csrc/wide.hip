@@ -10,7 +10,7 @@
 // compute-bound), so it is written as an LDS-tiled matrix product:
 //
 //  * one workgroup (8 waves) per tile of BV = 256 vocabulary rows by BM positions
-//    (BM = 128 or 256); the tiles of one vocabulary block go to the same XCD side
+//    (BM = 64, 128 or 256); the tiles of one vocabulary block go to the same XCD side
 //    by side, so after the first one its W comes from that XCD's L2;
 //  * both operands are staged in LDS in K-stages of 64 hidden elements (128 bytes
 //    per row) with 16-byte direct-to-LDS loads: one load instruction fills 1 KB,
@@ -408,10 +408,13 @@ hipError_t launch_bm(const Plan& plan, const LmHeadArgs& args, hipStream_t strea
 
 int wide_rows() { return BV; }
 
-size_t wide_lds_bytes(int bm) { return bm == 256 ? WideCfg<256>::LDS : WideCfg<128>::LDS; }
+size_t wide_lds_bytes(int bm) {
+    return bm == 256 ? WideCfg<256>::LDS : bm == 128 ? WideCfg<128>::LDS : WideCfg<64>::LDS;
+}
 
 hipError_t launch_wide(const Plan& plan, const LmHeadArgs& args, hipStream_t stream) {
     switch (plan.nt) {
+        case 64: return launch_bm<64>(plan, args, stream);
         case 128: return launch_bm<128>(plan, args, stream);
         case 256: return launch_bm<256>(plan, args, stream);
         default: return hipErrorInvalidConfiguration;
