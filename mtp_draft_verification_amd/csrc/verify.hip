@@ -12,9 +12,10 @@
 //
 // The draw itself (correction from normalize(max(0, p - q)) at the first
 // rejection, bonus from p_k after k acceptances, or a drafter draw from q)
-// runs in fp64 over the spilled fp32 logits in three passes over the one or two
-// rows a job needs: per-chunk sums of exp(l/T - ref) (the normaliser, in fp64,
-// recomputed here with the exact 1/T), per-64-token tile sums of the weights,
+// runs over the spilled fp32 logits in three passes over the one or two rows a
+// job needs, with fp64 sums: per-chunk sums of exp(l/T - ref) (the normaliser,
+// recomputed here with the exact 1/T from the same per-element values the weights
+// use), per-64-token tile sums of the weights,
 // and a search over those sums in a fixed order followed by a wave-level scan
 // inside the chosen tile. Every comparison uses sums built in one fixed order,
 // so the search is consistent and bit-reproducible.
@@ -279,8 +280,16 @@ __device__ __forceinline__ float row_logit(const float* logits, int row, int V, 
 }
 
 // exp(l / T - ref) in fp64 (0 for an element outside the row).
+// exp(l / T - ref) as 2^n * 2^f: t = (l / T - ref) log2(e) in fp64, n = round(t),
+// f = t - n in [-1/2, 1/2], 2^f from the hardware fp32 exp2 of f (f exact to 2^-25,
+// the result to about 1e-7 relative), scaled by 2^n exactly. The error is a small
+// random relative factor per element: the job's normaliser sums these same values,
+// so a common scale cancels, and the cumulative sums stay in fp64.
 __device__ __forceinline__ double row_exp_of(float l, bool live, double inv_t, double ref) {
-    return live ? exp(fma((double)l, inv_t, -ref)) : 0.0;
+    if (!live) return 0.0;
+    const double t = fma((double)l, inv_t, -ref) * 1.442695040888963407359924681001892137;
+    const double n = rint(t);
+    return ldexp((double)exp2f((float)(t - n)), (int)n);
 }
 
 // Weight of one element for a job from its two logits: max(0, p - q) with a drafter
