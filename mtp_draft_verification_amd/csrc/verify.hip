@@ -15,10 +15,10 @@
 // runs over the spilled fp32 logits in three passes over the one or two rows a
 // job needs, with fp64 sums: per-chunk sums of exp(l/T - ref) (the normaliser,
 // recomputed here with the exact 1/T from the same per-element values the weights
-// use), per-64-token tile sums of the weights,
-// and a search over those sums in a fixed order followed by a wave-level scan
-// inside the chosen tile. Every comparison uses sums built in one fixed order,
-// so the search is consistent and bit-reproducible.
+// use), per-64-token tile sums of the weights, and a search over those sums in a
+// fixed order followed by a scan inside the chosen tile in the same order as its
+// tile sum. Every comparison uses sums built in one fixed order, so the search is
+// consistent and bit-reproducible.
 #include "mtpv_internal.h"
 
 #include <climits>
@@ -274,12 +274,30 @@ __device__ __forceinline__ double wave_sum(double v) {
     return v;
 }
 
-// Logit of element v of `row` (0 past V or for row < 0; such elements get weight 0).
-__device__ __forceinline__ float row_logit(const float* logits, int row, int V, int v) {
-    return (row < 0 || v >= V) ? 0.f : logits[(size_t)row * V + v];
+// Four consecutive logits of `row` from token v (v % 4 == 0): one 16-byte load when
+// rows are 16-byte aligned (V % 4 == 0), else four loads. Addresses are clamped into
+// the row, so tokens at or past V (and rows < 0) read some logit of the row; callers
+// give those tokens weight 0.
+struct F4 {
+    float a[4];
+};
+
+__device__ __forceinline__ F4 row_logit4(const float* logits, int row, int V, int v) {
+    const float* base = logits + (size_t)max(row, 0) * V;
+    F4 r;
+    if ((V & 3) == 0) {
+        const float4 x = *reinterpret_cast<const float4*>(base + min(v, V - 4));
+        r.a[0] = x.x;
+        r.a[1] = x.y;
+        r.a[2] = x.z;
+        r.a[3] = x.w;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r.a[e] = base[min(v + e, V - 1)];
+    }
+    return r;
 }
 
-// exp(l / T - ref) in fp64 (0 for an element outside the row).
 // exp(l / T - ref) as 2^n * 2^f: t = (l / T - ref) log2(e) in fp64, n = round(t),
 // f = t - n in [-1/2, 1/2], 2^f from the hardware fp32 exp2 of f (f exact to 2^-25,
 // the result to about 1e-7 relative), scaled by 2^n exactly. The error is a small
@@ -303,27 +321,31 @@ __device__ __forceinline__ double weight_of(float lp, float lq, bool live, bool 
     return d > 0.0 ? d : 0.0;
 }
 
-__device__ __forceinline__ double job_weight(const float* logits, const Job& job, bool use_q, int V, int v,
-                                             double inv_t, double rp, double rq) {
-    const float lp = row_logit(logits, job.row_p, V, v);
-    const float lq = use_q ? row_logit(logits, job.row_q, V, v) : 0.f;
-    return weight_of(lp, lq, v < V, use_q, inv_t, job, rp, rq);
+// The fixed order of a 64-token tile, shared by the tile-sum pass and the search:
+// lane q of a 16-lane group holds tokens 4q .. 4q + 3 of the tile, sums them in token
+// order (w0 + w1) + w2 + w3, and the group takes the inclusive scan of those lane
+// sums (Hillis-Steele, 16 lanes). The tile total is lane 15's scan value.
+struct Lane4 {
+    double w[4];
+    double s;  // ((w0 + w1) + w2) + w3
+};
+
+__device__ __forceinline__ Lane4 lane_weights(const F4& lp, const F4& lq, int v, int vend, bool use_q, double inv_t,
+                                              const Job& job, double rp, double rq) {
+    Lane4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r.w[e] = weight_of(lp.a[e], lq.a[e], v + e < vend, use_q, inv_t, job, rp, rq);
+    r.s = ((r.w[0] + r.w[1]) + r.w[2]) + r.w[3];
+    return r;
 }
 
-// Inclusive scan of one 64-token tile's weights in lane order, lane i holding the
-// weight of token tile * 64 + i.
-__device__ __forceinline__ double lane_scan(double x, int lane) {
+__device__ __forceinline__ double scan16(double x, int q) {
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const double y = __shfl_up(x, off);
-        if (lane >= off) x += y;
+    for (int off = 1; off < 16; off <<= 1) {
+        const double y = __shfl_up(x, off, 16);
+        if (q >= off) x += y;
     }
     return x;
-}
-
-__device__ __forceinline__ double tile_scan(const float* logits, const Job& job, bool use_q, int V, int tile,
-                                            double inv_t, double rp, double rq, int lane) {
-    return lane_scan(job_weight(logits, job, use_q, V, tile * 64 + lane, inv_t, rp, rq), lane);
 }
 
 // Reciprocals of the job's normalisers (sums of the fixed-order chunk partials).
@@ -338,9 +360,9 @@ __device__ __forceinline__ void normalisers(const ResidualArgs& p, int j, double
     *rq = 1.0 / b;
 }
 
-// Tokens per thread and loop trip in the sampling passes: the loads of all of them
-// are issued before the fp64 arithmetic, so each thread keeps 2 * UR loads in flight.
-constexpr int UR = 8;
+// 16-byte loads per lane and row per loop trip in the sampling passes: all of them are
+// issued before the fp64 arithmetic.
+constexpr int UR = 4;
 
 // Pass 1: per-chunk sums of exp(l/T - ref) for the job's p row and q row.
 __global__ __launch_bounds__(256) void zsum_kernel(ResidualArgs p) {
@@ -354,19 +376,23 @@ __global__ __launch_bounds__(256) void zsum_kernel(ResidualArgs p) {
     const int e1 = min(p.V, t1 * 64);
     const bool has_q = job.row_q >= 0;
     double sp = 0.0, sq = 0.0;
-    for (int base = t0 * 64; base < e1; base += 256 * UR) {
-        float lp[UR], lq[UR];
+    for (int base = t0 * 64; base < e1; base += 1024 * UR) {
+        F4 lp[UR], lq[UR];
 #pragma unroll
         for (int i = 0; i < UR; ++i) {
-            const int v = base + 256 * i + tid;
-            lp[i] = v < e1 ? row_logit(p.logits, job.row_p, p.V, v) : 0.f;
-            lq[i] = v < e1 ? row_logit(p.logits, job.row_q, p.V, v) : 0.f;
+            const int v = base + 1024 * i + 4 * tid;
+            lp[i] = row_logit4(p.logits, job.row_p, p.V, v);
+            lq[i] = row_logit4(p.logits, has_q ? job.row_q : job.row_p, p.V, v);
         }
 #pragma unroll
         for (int i = 0; i < UR; ++i) {
-            const bool live = base + 256 * i + tid < e1;
-            sp += row_exp_of(lp[i], live && job.row_p >= 0, p.inv_t, job.ref_p);
-            sq += row_exp_of(lq[i], live && has_q, p.inv_t, job.ref_q);
+            const int v = base + 1024 * i + 4 * tid;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool live = v + e < e1;
+                sp += row_exp_of(lp[i].a[e], live, p.inv_t, job.ref_p);
+                sq += row_exp_of(lq[i].a[e], live && has_q, p.inv_t, job.ref_q);
+            }
         }
     }
     sp = wave_sum(sp);
@@ -383,34 +409,33 @@ __global__ __launch_bounds__(256) void zsum_kernel(ResidualArgs p) {
     }
 }
 
-// Pass 2: per-tile sums of the job's weights (the lane-order scan's last value, the
-// same arithmetic the search pass repeats on the tile it lands in).
+// Pass 2: per-tile sums of the job's weights in the tile's fixed order. Each wave
+// load covers four consecutive tiles (1 KB of each row); wave w of the workgroup takes
+// tiles 4 w .. 4 w + 3 of every 16.
 __global__ __launch_bounds__(256) void tsum_kernel(ResidualArgs p) {
     const int j = blockIdx.y, c = blockIdx.x;
     const Job job = p.jobs[j];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, q = lane & 15;
     double rp, rq;
     normalisers(p, j, &rp, &rq);
     const bool use_q = job.row_q >= 0;
     const int tpc = (p.ntiles + p.C - 1) / p.C;
     const int t0 = c * tpc, t1 = min(p.ntiles, t0 + tpc);
-    for (int tb = t0 + wave; tb < t1; tb += 4 * UR) {
-        float lp[UR], lq[UR];
+    for (int tb = t0 + 4 * wave + g; tb < t1; tb += 16 * UR) {  // uniform within each 16-lane group
+        F4 lp[UR], lq[UR];
 #pragma unroll
         for (int i = 0; i < UR; ++i) {
-            const int t = tb + 4 * i;
-            const int v = t * 64 + lane;
-            lp[i] = t < t1 ? row_logit(p.logits, job.row_p, p.V, v) : 0.f;
-            lq[i] = (t < t1 && use_q) ? row_logit(p.logits, job.row_q, p.V, v) : 0.f;
+            const int v = (tb + 16 * i) * 64 + 4 * q;
+            lp[i] = row_logit4(p.logits, job.row_p, p.V, v);
+            lq[i] = row_logit4(p.logits, use_q ? job.row_q : job.row_p, p.V, v);
         }
 #pragma unroll
         for (int i = 0; i < UR; ++i) {
-            const int t = tb + 4 * i;
-            if (t < t1) {  // uniform over the wave
-                const double w = weight_of(lp[i], lq[i], t * 64 + lane < p.V, use_q, p.inv_t, job, rp, rq);
-                const double incl = lane_scan(w, lane);
-                if (lane == 63) p.tsum[(size_t)j * p.ntiles + t] = incl;
-            }
+            const int t = tb + 16 * i;
+            const Lane4 w = lane_weights(lp[i], lq[i], t * 64 + 4 * q, p.V, use_q, p.inv_t, job, rp, rq);
+            const double incl = scan16(w.s, q);
+            if (q == 15 && t < t1) p.tsum[(size_t)j * p.ntiles + t] = incl;
         }
     }
 }
@@ -434,10 +459,15 @@ __global__ __launch_bounds__(256) void search_kernel(ResidualArgs p) {
 
     for (int pass = 0; pass < 2; ++pass) {
         if (pass == 1) {
-            // Residual mass was zero: draw from p instead (tile sums rebuilt for p).
-            for (int t = wave; t < p.ntiles; t += 4) {
-                const double incl = tile_scan(p.logits, job, false, p.V, t, p.inv_t, rp, rq, lane);
-                if (lane == 63) ts[t] = incl;
+            // Residual mass was zero: draw from p instead (tile sums rebuilt for p,
+            // in the tile order of the tile-sum pass).
+            const int g = lane >> 4, q = lane & 15;
+            for (int tb = 4 * wave + g; tb < p.ntiles; tb += 16) {  // uniform within each 16-lane group
+                const int v = tb * 64 + 4 * q;
+                const F4 lp = row_logit4(p.logits, job.row_p, p.V, v);
+                const Lane4 w = lane_weights(lp, lp, v, p.V, false, p.inv_t, job, rp, rq);
+                const double incl = scan16(w.s, q);
+                if (q == 15 && tb < p.ntiles) ts[tb] = incl;
             }
             __syncthreads();
         }
@@ -501,15 +531,38 @@ __global__ __launch_bounds__(256) void search_kernel(ResidualArgs p) {
             continue;
         }
         if (wave == 0) {
-            const double incl = tile_scan(p.logits, job, use_q, p.V, sh_tile, p.inv_t, rp, rq, lane);
-            const double w = job_weight(p.logits, job, use_q, p.V, sh_tile * 64 + lane, p.inv_t, rp, rq);
-            const unsigned long long hit = __ballot(sh_base + incl > sh_target);
-            const unsigned long long pos = __ballot(w > 0.0);
-            int ln;
-            if (hit) ln = __ffsll(hit) - 1;
-            else if (pos) ln = 63 - __clzll(pos);
-            else ln = 0;
-            if (lane == 0) p.out[job.out_index] = min(sh_tile * 64 + ln, p.V - 1);
+            // the chosen tile in the tile-sum pass's order: lanes 0..15 hold 4 tokens each
+            // (lanes 16..63 repeat the computation and are left out of the ballots)
+            const int q = lane & 15;
+            const int v = sh_tile * 64 + 4 * q;
+            const F4 lp = row_logit4(p.logits, job.row_p, p.V, v);
+            const F4 lq = row_logit4(p.logits, use_q ? job.row_q : job.row_p, p.V, v);
+            const Lane4 w = lane_weights(lp, lq, v, p.V, use_q, p.inv_t, job, rp, rq);
+            const double incl = scan16(w.s, q);
+            double excl = __shfl_up(incl, 1, 16);
+            if (q == 0) excl = 0.0;
+            // cumulative weight through each token of the lane: the scan value of the
+            // lane before, plus the lane's partial sums in token order; the lane's last
+            // token takes its own scan value, so the tile's last token carries exactly
+            // the tile total the walk compared
+            const double b = sh_base, tg = sh_target;
+            const double c0 = excl + w.w[0];
+            const double c1 = excl + (w.w[0] + w.w[1]);
+            const double c2 = excl + ((w.w[0] + w.w[1]) + w.w[2]);
+            const int first = (b + c0 > tg) ? 0 : (b + c1 > tg) ? 1 : (b + c2 > tg) ? 2 : (b + incl > tg) ? 3 : 4;
+            const int lastpos = w.w[3] > 0.0 ? 3 : w.w[2] > 0.0 ? 2 : w.w[1] > 0.0 ? 1 : w.w[0] > 0.0 ? 0 : -1;
+            const unsigned long long group = 0xFFFFull;
+            const unsigned long long hit = __ballot(first < 4) & group;
+            const unsigned long long pos = __ballot(lastpos >= 0) & group;
+            int ln = 0, e = 0;
+            if (hit) {
+                ln = __ffsll(hit) - 1;
+                e = __shfl(first, ln);
+            } else if (pos) {  // rounding left the target past the tile: its last positive token
+                ln = 63 - __clzll(pos);
+                e = __shfl(lastpos, ln);
+            }
+            if (lane == 0) p.out[job.out_index] = min(sh_tile * 64 + 4 * ln + e, p.V - 1);
         }
         break;
     }
