@@ -348,6 +348,15 @@ __device__ __forceinline__ double scan16(double x, int q) {
     return x;
 }
 
+__device__ __forceinline__ double wave_scan(double x, int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const double y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
 // Reciprocals of the job's normalisers (sums of the fixed-order chunk partials).
 __device__ __forceinline__ void normalisers(const ResidualArgs& p, int j, double* rp, double* rq) {
     double a = 0.0, b = 0.0;
@@ -442,11 +451,10 @@ __global__ __launch_bounds__(256) void tsum_kernel(ResidualArgs p) {
 
 // Pass 3: locate u * (total weight) in the fixed-order sums and emit the token.
 __global__ __launch_bounds__(256) void search_kernel(ResidualArgs p) {
-    __shared__ double thread_tot[256];
-    __shared__ int sh_tile;
+    __shared__ double wave_tot[4];
+    __shared__ int sh_tile, sh_last, sh_pick;
     __shared__ double sh_base;
     __shared__ double sh_target;
-    __shared__ int sh_retry;
     const int j = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -471,70 +479,81 @@ __global__ __launch_bounds__(256) void search_kernel(ResidualArgs p) {
             }
             __syncthreads();
         }
+        // Each thread owns a run of consecutive tiles and sums it in tile order; a block
+        // scan of the run totals gives every run its starting point, so each thread can
+        // walk its own tiles from there. The first tile (over all threads) whose running
+        // sum passes the target is the draw's tile; its base is the running sum before it.
+        const int i0 = min(p.ntiles, tid * per), i1 = min(p.ntiles, i0 + per);
         double tot = 0.0;
-        for (int i = tid * per; i < min(p.ntiles, (tid + 1) * per); ++i) tot += ts[i];
-        thread_tot[tid] = tot;
-        __syncthreads();
+        int lastpos_tile = -1;
+        for (int i = i0; i < i1; ++i) {
+            const double t = ts[i];
+            tot += t;
+            if (t > 0.0) lastpos_tile = i;
+        }
+        const double incl = wave_scan(tot, lane);
+        double excl = __shfl_up(incl, 1);
+        if (lane == 0) excl = 0.0;
+        if (lane == 63) wave_tot[wave] = incl;
         if (tid == 0) {
-            double R = 0.0;
-            for (int t = 0; t < 256; ++t) R += thread_tot[t];
-            sh_retry = 0;
-            if (!(R > 0.0)) {
-                sh_retry = (pass == 0 && use_q) ? 1 : 0;
-                sh_tile = 0;
+            sh_tile = INT_MAX;
+            sh_last = -1;
+        }
+        __syncthreads();
+        double R = 0.0, wbase = 0.0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            if (w == wave) wbase = R;
+            R += wave_tot[w];
+        }
+        if (!(R > 0.0)) {
+            if (pass == 0 && use_q) {  // residual mass is zero: draw from p (uniform over the block)
+                use_q = false;
+                __syncthreads();
+                continue;
+            }
+            // degenerate: every weight is zero; take token 0
+            if (tid == 0) {
+                sh_pick = 0;
                 sh_base = 0.0;
-                sh_target = -1.0;  // degenerate: every weight is zero; take token 0
-            } else {
-                // Skip whole thread ranges while their fixed-order totals stay at or
-                // below the target, then walk tiles one by one from there. The walk may
-                // run past that range: a range total and the running sum of its tiles
-                // associate differently and can differ in the last bit.
-                const double target = job.u * R;
-                double run = 0.0;
-                int tt = -1;
-                for (int t = 0; t < 256; ++t) {
-                    if (run + thread_tot[t] > target) {
-                        tt = t;
-                        break;
-                    }
-                    run += thread_tot[t];
+                sh_target = -1.0;
+            }
+        } else {
+            const double target = job.u * R;
+            double run = wbase + excl;
+            int cand = -1;
+            for (int i = i0; i < i1; ++i) {
+                const double t = ts[i];
+                if (run + t > target) {
+                    cand = i;
+                    atomicMin(&sh_tile, i);
+                    break;
                 }
-                if (tt < 0) {
-                    tt = 0;
-                    run = 0.0;
+                run += t;
+            }
+            if (lastpos_tile >= 0) atomicMax(&sh_last, lastpos_tile);
+            __syncthreads();
+            const int tile = sh_tile;
+            if (tile == INT_MAX) {
+                // rounding put the target past the end: the last tile with mass, searched
+                // with a target no prefix reaches, which selects its last positive token
+                if (tid == 0) {
+                    sh_pick = sh_last;
+                    sh_base = 0.0;
+                    sh_target = __builtin_huge_val();
                 }
-                int found = -1;
-                for (int i = tt * per; i < p.ntiles; ++i) {
-                    if (run + ts[i] > target) {
-                        found = i;
-                        break;
-                    }
-                    run += ts[i];
-                }
-                if (found < 0) {  // rounding put the target past the end: last tile with mass
-                    int last = 0;
-                    for (int i = 0; i < p.ntiles; ++i)
-                        if (ts[i] > 0.0) last = i;
-                    run = 0.0;
-                    for (int i = 0; i < last; ++i) run += ts[i];
-                    found = last;
-                }
-                sh_tile = found;
+            } else if (cand == tile) {  // the one thread whose walk stopped there
+                sh_pick = tile;
                 sh_base = run;
                 sh_target = target;
             }
         }
         __syncthreads();
-        if (sh_retry) {
-            use_q = false;
-            __syncthreads();
-            continue;
-        }
         if (wave == 0) {
             // the chosen tile in the tile-sum pass's order: lanes 0..15 hold 4 tokens each
             // (lanes 16..63 repeat the computation and are left out of the ballots)
             const int q = lane & 15;
-            const int v = sh_tile * 64 + 4 * q;
+            const int v = sh_pick * 64 + 4 * q;
             const F4 lp = row_logit4(p.logits, job.row_p, p.V, v);
             const F4 lq = row_logit4(p.logits, use_q ? job.row_q : job.row_p, p.V, v);
             const Lane4 w = lane_weights(lp, lq, v, p.V, use_q, p.inv_t, job, rp, rq);
@@ -562,7 +581,7 @@ __global__ __launch_bounds__(256) void search_kernel(ResidualArgs p) {
                 ln = 63 - __clzll(pos);
                 e = __shfl(lastpos, ln);
             }
-            if (lane == 0) p.out[job.out_index] = min(sh_tile * 64 + 4 * ln + e, p.V - 1);
+            if (lane == 0) p.out[job.out_index] = min(sh_pick * 64 + 4 * ln + e, p.V - 1);
         }
         break;
     }
