@@ -39,6 +39,8 @@ Layers:
   random numbers          : philox.philox4x32_10, philox.verify_uniforms
   metrics                 : metrics.acceptance_metrics
   MTP input fusion        : mtp_input.rms_norm, fused_input, mtp_input_fuse
+  top-k soft-CE draft loss: draft_loss.topk_teacher, soft_targets, draft_loss,
+                            draft_loss_grad
 
 Every function is pinned by a `-m "not gpu"` test against something other than
 itself (exact rational enumeration, closed forms, library routines, an
@@ -64,6 +66,7 @@ from .verify import (
     verify_sample_ragged_from_hidden,
 )
 from .mtp_input import rms_norm, fused_input, mtp_input_fuse
+from .draft_loss import topk_teacher, soft_targets, draft_loss, draft_loss_grad, draft_loss_row
 from .philox import philox4x32_10, uniform24, verify_uniforms
 from .metrics import acceptance_metrics
 
@@ -74,5 +77,6 @@ __all__ = [
     "greedy_verify_ragged", "stochastic_verify_ragged", "verify_greedy_ragged_from_hidden",
     "verify_sample_ragged_from_hidden",
     "rms_norm", "fused_input", "mtp_input_fuse",
+    "topk_teacher", "soft_targets", "draft_loss", "draft_loss_grad", "draft_loss_row",
     "philox4x32_10", "uniform24", "verify_uniforms", "acceptance_metrics",
 ]

@@ -154,3 +154,33 @@ def fuse_inputs(H, V, B, cid=300, step=0, embed=True):
     W_fc = round_to_bf16(_rng(cid, 7, 0).standard_normal((H, 2 * H), dtype=np.float32) * np.float32(0.02))
     tokens = _rng(cid, 8, step).integers(0, V, size=B).astype(np.int32)
     return tokens, E, h, round_to_bf16(g[0]), round_to_bf16(g[1]), W_fc
+
+
+def loss_rows(V, rows, cid=400, step=0, t_std=3.0, s_noise=1.0, quantum=None):
+    """Seeded fp32 logits of the draft-loss workload, one generator per row (so any
+    subset of rows of a large call can be rebuilt alone):
+    stream 9, key (cid, 9, step, n): teacher row T[n] ~ N(0, 1) * t_std, rounded to a
+              multiple of `quantum` when given (many equal logits);
+    stream 10, key (cid, 10, step, n): student row S[n] = T[n] + N(0, 1) * s_noise.
+    Returns (T, S) of shape [len(rows), V].
+    """
+    rows = list(rows)
+    T = np.empty((len(rows), V), dtype=np.float32)
+    S = np.empty((len(rows), V), dtype=np.float32)
+
+    def fill(i):
+        n = rows[i]
+        t = _rng(cid, 9, step, n).standard_normal(V, dtype=np.float32) * np.float32(t_std)
+        if quantum is not None:
+            t = (np.round(t / np.float32(quantum)) * np.float32(quantum)).astype(np.float32)
+        T[i] = t
+        S[i] = t + _rng(cid, 10, step, n).standard_normal(V, dtype=np.float32) * np.float32(s_noise)
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(fill, range(len(rows))))
+    return T, S
+
+
+def loss_inputs(N, V, cid=400, step=0, **kw):
+    """All N rows of the draft-loss workload (loss_rows over 0..N-1)."""
+    return loss_rows(V, range(N), cid, step, **kw)
