@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--mode greedy|sample]
     python bench.py --op fuse --workload 3     (MTP input fusion at that width and batch)
+    python bench.py --op loss                  (top-k soft cross-entropy draft loss + gradient)
     python bench.py --sweep                    (greedy verify time against M_eff, one line per M)
 
 One step = one verify call (the whole hot path: LM-head stream + fused softmax/argmax
@@ -79,14 +80,18 @@ def algorithmic(wl, mode):
     return bytes_, flops
 
 
+def _blas_cores():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(wl, mode, W_store, budget_s):
     """The oracle as it stands, on this host's cores, over a bounded number of steps."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = os.cpu_count() or 1
+    cores = _blas_cores()
     decode = oracle.decode_bf16 if wl.dtype == "bf16" else (lambda a: np.asarray(a, dtype=np.float64))
     W64 = decode(W_store)
     n = 0
@@ -198,6 +203,56 @@ def bench_fuse(args, wl):
     print(json.dumps(line), flush=True)
 
 
+def bench_loss(args):
+    """Top-k soft cross-entropy draft loss with its gradient: teacher and student fp32
+    logits [N, V] resident in HBM, one call = selection pass (loss, kept ids) +
+    gradient pass. The dominant kernel is the selection pass (both rows streamed
+    once); the call as a whole reads the student row a second time for the gradient."""
+    import torch
+    import mtp_draft_verification_amd as mv
+    import oracle
+    dev = torch.device("cuda:0")
+    N, V, k = args.loss_rows, 151936, args.topk
+    log(f"loss: generating teacher/student logits [{N}, {V}] fp32")
+    T, S = synth.loss_inputs(N, V, cid=420)
+    Td = torch.from_numpy(T).to(dev)
+    Sd = torch.from_numpy(S).to(dev)
+    loss = torch.empty(N, dtype=torch.float32, device=dev)
+    idx = torch.empty((N, k), dtype=torch.int32, device=dev)
+    grad = torch.empty((N, V), dtype=torch.float32, device=dev)
+    ws = mv.alloc_loss_workspace(N, k, dev)
+    scale = 1.0 / N
+
+    def call():
+        mv.mtp_draft_loss_topk(Td, Sd, k, loss, ws, scale, idx, grad)
+
+    wall, kern = _events_time(call, args.steps, args.warmup)
+    sel_bytes = N * V * 8 + N * 4 + N * k * 4            # teacher + student once, loss + kept ids
+    call_bytes = N * V * 12 + N * 4 + N * k * 4          # ... + the gradient written once
+    line = {"metric": "draft-loss rows/s (top-k soft cross-entropy, loss + gradient)",
+            "value": round(N / wall, 1), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded N(0,1)*3 teacher, "
+            "student = teacher + N(0,1))",
+            "config": {"workload": f"draft_loss_N{N}_V{V}_topk{k}", "N": N, "V": V, "topk": k, "grad": True},
+            "roofline": {"bound": "hbm", "achieved": round(sel_bytes / kern / 1e9, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(sel_bytes / kern / 1e9 / HBM_PEAK_GBS, 4),
+                         "traffic": None, "kernel_us": round(kern * 1e6, 2),
+                         "algorithmic_bytes_per_launch": sel_bytes,
+                         "call_frac": round(call_bytes / wall / 1e9 / HBM_PEAK_GBS, 4)}}
+    if not args.no_cpu_baseline:
+        rows, el = 0, 0.0
+        while el < args.cpu_budget and rows < N:
+            t0 = time.perf_counter()
+            oracle.draft_loss(T[rows:rows + 1], S[rows:rows + 1], k)
+            oracle.draft_loss_grad(T[rows:rows + 1], S[rows:rows + 1], k, scale)
+            el += time.perf_counter() - t0
+            rows += 1
+        line["cpu_baseline"] = {"value": round(rows / el, 2), "unit": "rows/s", "cores": _blas_cores(),
+                                "kind": "oracle", "sample": f"{rows} rows of the same call (loss + gradient)"}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -211,8 +266,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run the library's plain copy kernel on this many MiB (counter calibration)")
-    ap.add_argument("--op", choices=["verify", "fuse"], default="verify",
-                    help="verify (default) or the MTP input fusion at the workload's H and B")
+    ap.add_argument("--op", choices=["verify", "fuse", "loss"], default="verify",
+                    help="verify (default), the MTP input fusion at the workload's H and B, or the top-k "
+                         "soft cross-entropy draft loss")
+    ap.add_argument("--loss-rows", type=int, default=4096, help="rows (token positions) of the draft loss")
+    ap.add_argument("--topk", type=int, default=256, help="teacher tokens kept by the draft loss")
     ap.add_argument("--sweep", action="store_true",
                     help="greedy verify time against M_eff at H=5120, V=151936 (one JSON line per M)")
     args = ap.parse_args()
@@ -228,6 +286,8 @@ def main():
 
     if args.sweep:
         return sweep(args)
+    if args.op == "loss":
+        return bench_loss(args)
     wl = synth.WORKLOADS[args.workload]
     if args.op == "fuse":
         return bench_fuse(args, wl)

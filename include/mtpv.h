@@ -246,6 +246,33 @@ MTPV_API int mtp_input_fuse(const int32_t* tokens, const void* embed, const void
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Top-k soft cross-entropy draft loss ("Faster Rollouts with MTP Speculative
+ * Decoding", SkyRL docs, sections "Overview" and "How does it work?": the MTP head is
+ * trained toward the detached policy's next-token distribution with a soft
+ * cross-entropy over the policy's top-k tokens; k = 256 in the section "Example").
+ * The page prints no formula; the reading is, per row n:
+ *   K       = the topk tokens with the largest teacher logits (equal logits: lower
+ *             token id first; -0.0 and +0.0 are equal)
+ *   pt_j    = softmax over the kept teacher logits (j in K)
+ *   loss[n] = logsumexp_v(student[n, v]) - sum_{j in K} pt_j * student[n, j]
+ *   grad    = grad_scale * (softmax(student[n]) - pt scattered on K)
+ * teacher, student [N, V] fp32 row-major (device); loss [N] fp32 (device, output);
+ * topk_index [N, topk] int32 (device, output, may be NULL): the kept ids, largest
+ * teacher logit first; grad [N, V] fp32 (device, output, may be NULL: no gradient
+ * pass). 1 <= topk <= min(V, MTPV_LOSS_MAX_TOPK); N >= 0 (N = 0 does nothing);
+ * V <= 2^30. Logits must not be NaN, and every student row needs a finite logit.
+ * Rows whose start is 16-byte aligned (V % 4 == 0, aligned bases) take 16-byte loads.
+ * Workspace: mtpv_loss_workspace_bytes(N, topk), 256-byte aligned, caller-owned;
+ * its contents are scratch. Errors: MTPV_EINVAL (sizes, non-finite grad_scale),
+ * MTPV_ENULL, MTPV_EALIGN (a pointer not 4-byte aligned), MTPV_EWORKSPACE.
+ */
+#define MTPV_LOSS_MAX_TOPK 512
+MTPV_API size_t mtpv_loss_workspace_bytes(int N, int topk);
+MTPV_API int mtp_draft_loss_topk(const float* teacher, const float* student, int N, int V, int topk,
+                            float grad_scale, float* loss, int32_t* topk_index, float* grad,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Drafter-side sampling through the same shared head: for each request b and
  * drafter row j (0..kd-1), draft_tokens[b*kd + j] ~ softmax(l(drafter row) / T),
  * drawn by inverse transform with uniform(word 2 of Philox(seed; depth0 + j, b,

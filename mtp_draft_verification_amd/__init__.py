@@ -15,6 +15,8 @@ Calls (names as in the C ABI):
                    accepted_len_greedy, out_tokens_greedy, accepted_len_sample, out_tokens_sample, workspace)
   mtp_input_fuse(tokens[B], embed[V,H], hidden[B,H], norm_emb[H], norm_hidden[H], W_fc[H,2H], eps, out[B,H],
                  workspace)
+  mtp_draft_loss_topk(teacher[N,V], student[N,V], topk, loss[N], workspace, grad_scale, topk_index[N,topk],
+                      grad[N,V])   top-k soft cross-entropy draft loss (fp32 logits)
 """
 import ctypes
 import os
@@ -27,6 +29,7 @@ DTYPE_BF16, DTYPE_F32 = 0, 1
 DEVERR_DRAFT_RANGE = 1
 DEVERR_DRAFT_LEN = 2
 DEVERR_TOKEN_RANGE = 4
+LOSS_MAX_TOPK = 512
 
 STATUS = {0: "MTPV_OK", -1: "MTPV_EINVAL", -2: "MTPV_EALIGN", -3: "MTPV_EWORKSPACE", -4: "MTPV_EDTYPE",
           -5: "MTPV_ENULL", -6: "MTPV_ELAUNCH", -7: "MTPV_EDEVICE"}
@@ -65,6 +68,8 @@ _SIGNATURES = {
                               _vp, _sz, _vp, _vp]),
     "mtpv_fuse_workspace_bytes": (_sz, [_i, _i]),
     "mtp_input_fuse": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _d, _vp, _vp, _sz, _vp]),
+    "mtpv_loss_workspace_bytes": (_sz, [_i, _i]),
+    "mtp_draft_loss_topk": (_i, [_vp, _vp, _i, _i, _i, ctypes.c_float, _vp, _vp, _vp, _vp, _sz, _vp]),
     "mtpv_device_error": (_i, [_vp, ctypes.POINTER(ctypes.c_int32), _vp]),
     "mtpv_timing_enable": (_i, [_i]),
     "mtpv_timing_read": (_i, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), _i]),
@@ -248,6 +253,31 @@ def mtp_input_fuse(tokens, embed, hidden, norm_emb, norm_hidden, W_fc, eps, out,
     st = lib().mtp_input_fuse(_ptr(tokens), _ptr(embed), _ptr(hidden), _ptr(norm_emb), _ptr(norm_hidden), _ptr(W_fc),
                               B, H, V, float(eps), _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "mtp_input_fuse")
+
+
+def alloc_loss_workspace(N, topk, device):
+    import torch
+    n = lib().mtpv_loss_workspace_bytes(N, topk)
+    if n == 0:
+        raise MtpvError(-1, "mtpv_loss_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def mtp_draft_loss_topk(teacher, student, topk, loss, workspace, grad_scale=1.0, topk_index=None, grad=None,
+                        stream=None):
+    """Top-k soft cross-entropy draft loss: teacher, student [N,V] fp32 -> loss [N] fp32; optionally the
+    kept teacher ids topk_index [N,topk] int32 (best first) and grad [N,V] fp32 = d(grad_scale*loss)/d student."""
+    N, V = teacher.shape
+    for n, t in (("teacher", teacher), ("student", student), ("loss", loss), ("workspace", workspace),
+                 ("topk_index", topk_index), ("grad", grad)):
+        if t is not None:
+            _contig(n, t)
+    if tuple(student.shape) != (N, V):
+        raise ValueError("student must have the teacher's shape")
+    st = lib().mtp_draft_loss_topk(_ptr(teacher), _ptr(student), N, V, int(topk), float(grad_scale), _ptr(loss),
+                                   _ptr(topk_index), _ptr(grad), _ptr(workspace), workspace.numel(),
+                                   _stream(stream))
+    _check(st, "mtp_draft_loss_topk")
 
 
 def spec_draft_sample(draft_hidden, W, temperature, seed, offset, depth0, draft_tokens, workspace, debug=None,

@@ -220,6 +220,15 @@ int run(const Plan& plan, const void* xt, const void* xd, const void* w, const i
 }
 
 }  // namespace
+
+bool timed_launch_events(hipEvent_t* start, hipEvent_t* stop) {
+    std::pair<hipEvent_t, hipEvent_t>* ev = timing_slot();
+    if (ev == nullptr) return false;
+    *start = ev->first;
+    *stop = ev->second;
+    return true;
+}
+
 }  // namespace mtpv
 
 using namespace mtpv;

@@ -1,0 +1,514 @@
+// Top-k soft cross-entropy draft loss ("Faster Rollouts with MTP Speculative
+// Decoding", SkyRL docs, sections "Overview" and "How does it work?": the MTP head is
+// distilled toward the detached policy's next-token distribution with a soft
+// cross-entropy over the policy's top-k tokens, k = 256 in the section "Example").
+// Per row n of teacher logits t and student logits s over the vocabulary:
+//   K      = the k largest t (equal logits: lower index first; -0.0 equals +0.0)
+//   pt_j   = exp(t_j) / sum_{i in K} exp(t_i)           (j in K)
+//   loss_n = logsumexp_v(s) - sum_{j in K} pt_j s_j      (= - sum pt_j log q_j)
+//   grad   = scale * (softmax(s) - pt scattered on K)   (the teacher gets none)
+//
+// Selection kernel: one workgroup (4 waves) per row streams the teacher row and the
+// student row once with 16-byte loads. Each wave keeps, in LDS, the entries of its
+// share that beat a running threshold (the smallest entry it has kept); when its
+// buffer nears full it keeps only its k best (a bitwise search for the k-th key over
+// registers, ties by index) and raises the threshold; a plain float compare against
+// the threshold's value screens each token first. The student side keeps a per-lane
+// running maximum and an fp64 sum of exp(s - max) (hardware exp2 of the scaled
+// difference, summed in fp32 per 4 tokens). At the end the four
+// waves' lists are merged and cut to k, ranked, and the soft targets, the gathered
+// student logits and the loss are reduced in fp64 in a fixed order.
+//
+// Gradient (optional): a second streaming pass over the student rows writes
+// scale * (exp(s - lse) - pt) for every token (pt = 0 off the kept list), each chunk
+// of a row first marking its kept tokens in LDS.
+#include "mtpv.h"
+#include "mtpv_internal.h"
+
+#include <climits>
+#include <cmath>
+
+namespace mtpv {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kCap = 1248;                 // entries per wave buffer
+constexpr int kRoom = 256;                 // most entries one pass can add (64 lanes x 4)
+constexpr int kDepth = 4;                  // passes of loads in flight per wave
+constexpr int kPerWave = (kCap + 63) / 64; // buffer entries per lane when a wave compacts
+constexpr int kPerMerge = kWaves * MTPV_LOSS_MAX_TOPK / 64;
+static_assert(kCap - kRoom >= MTPV_LOSS_MAX_TOPK + 256, "room between compactions");
+static_assert(kWaves * kCap >= kWaves * MTPV_LOSS_MAX_TOPK + MTPV_LOSS_MAX_TOPK, "merge and rank areas");
+
+// Monotone map of an fp32 value to an unsigned key (larger value, larger key);
+// -0.0 maps to the key of +0.0.
+__device__ __forceinline__ uint32_t order_key(float x) {
+    uint32_t b = __float_as_uint(x);
+    if (b == 0x80000000u) b = 0u;
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_value(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// (key, index) ordering: larger key first, then lower index
+__device__ __forceinline__ bool beats(uint32_t k, int i, uint32_t tk, int ti) {
+    return k > tk || (k == tk && i < ti);
+}
+
+__device__ __forceinline__ int lanes_below(unsigned long long m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+__device__ __forceinline__ int wave_max_int(int v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off));
+    return v;
+}
+
+// Keeps the `want` best entries (larger key, then lower index) among the first n of
+// (bk, bi), moved to positions [0, want) in no particular order, and returns the
+// worst kept entry in (tk, ti). Runs on one whole wave; n <= 64 * PER and
+// want <= n; every entry's key is above 0 (no NaN logits).
+template <int PER>
+__device__ void wave_keep(uint32_t* bk, int32_t* bi, int n, int want, int lane, uint32_t& tk, int& ti) {
+    uint32_t k[PER];
+    int id[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        const int pos = e * 64 + lane;
+        const bool ok = pos < n;
+        k[e] = ok ? bk[pos] : 0u;
+        id[e] = ok ? bi[pos] : INT_MAX;
+    }
+    // the want-th largest key, decided bit by bit from the top
+    uint32_t T = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t c = T | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) cnt += __popcll(__ballot(k[e] >= c));
+        if (cnt >= want) T = c;
+    }
+    int above = 0, ties = 0, tie_max = -1;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        above += __popcll(__ballot(k[e] > T));
+        const bool t = k[e] == T;
+        ties += __popcll(__ballot(t));
+        if (t) tie_max = max(tie_max, id[e]);
+    }
+    tie_max = wave_max_int(tie_max);
+    const int r = want - above;  // entries of key T to keep: the r lowest indices
+    int I = tie_max;
+    if (r < ties) {
+        int lo = 0, hi = tie_max;
+        while (lo < hi) {
+            const int mid = lo + ((hi - lo) >> 1);
+            int c = 0;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) c += __popcll(__ballot(k[e] == T && id[e] <= mid));
+            if (c >= r)
+                hi = mid;
+            else
+                lo = mid + 1;
+        }
+        I = lo;
+    }
+    int base = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        const bool s = k[e] > T || (k[e] == T && id[e] <= I);
+        const unsigned long long m = __ballot(s);
+        if (s) {
+            const int pos = base + lanes_below(m);
+            bk[pos] = k[e];
+            bi[pos] = id[e];
+        }
+        base += __popcll(m);
+    }
+    tk = T;
+    ti = I;
+}
+
+__device__ __forceinline__ double block_sum(double v, double* sh) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    const int wave = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sh[wave] = v;
+    __syncthreads();
+    return ((sh[0] + sh[1]) + sh[2]) + sh[3];
+}
+
+__device__ __forceinline__ float block_max(float v, float* sh) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    const int wave = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sh[wave] = v;
+    __syncthreads();
+    return fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
+}
+
+struct F4 {
+    float x[4];
+};
+
+// Four consecutive values of a row from token v; past the row's end the address is
+// clamped to its last values (callers mask tokens >= V), so the load is never
+// predicated and the loads of a ring stay in flight together.
+template <bool VEC>
+__device__ __forceinline__ F4 load4(const float* row, int v, int V) {
+    F4 r;
+    if (VEC) {
+        const float4 q = *reinterpret_cast<const float4*>(row + min(v, V - 4));
+        r.x[0] = q.x;
+        r.x[1] = q.y;
+        r.x[2] = q.z;
+        r.x[3] = q.w;
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r.x[j] = row[min(v + j, V - 1)];
+    }
+    return r;
+}
+
+// Per-wave state of the stream: the kept-entry count and the worst kept entry
+// (key tk, index ti; thr = its value, a cheap first test), and the lane's running
+// student maximum m with sum of exp(s - m).
+struct StreamState {
+    int cnt = 0;
+    uint32_t tk = 0u;
+    int ti = INT_MAX;
+    float thr = -INFINITY;
+    float m = -INFINITY;
+    double sum = 0.0;
+};
+
+constexpr float kLog2eF = 1.44269504088896340736f;
+
+// One pass of a wave: 4 teacher and 4 student values per lane from token v. CHECK:
+// the pass reaches past the row's end (tokens >= V are masked).
+template <bool CHECK>
+__device__ __forceinline__ void consume(const F4& t4, const F4& s4, int v, int V, int lane, uint32_t* bk,
+                                        int32_t* bi, int K, StreamState& st) {
+    // teacher: only a value >= the worst kept one can beat it
+    bool any = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) any |= t4.x[j] >= st.thr;
+    if (__ballot(any)) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t key = order_key(t4.x[j]);
+            const bool take = (!CHECK || v + j < V) && beats(key, v + j, st.tk, st.ti);
+            const unsigned long long mk = __ballot(take);
+            if (mk) {
+                if (take) {
+                    const int pos = st.cnt + lanes_below(mk);
+                    bk[pos] = key;
+                    bi[pos] = v + j;
+                }
+                st.cnt += __popcll(mk);
+            }
+        }
+        if (st.cnt > kCap - kRoom) {
+            wave_keep<kPerWave>(bk, bi, st.cnt, K, lane, st.tk, st.ti);
+            st.cnt = K;
+            st.thr = key_value(st.tk);
+        }
+    }
+    // student: running maximum, then exp2 of the scaled differences (<= 0)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        if (!CHECK || v + j < V) mx = fmaxf(mx, s4.x[j]);
+    if (mx > st.m) {
+        if (st.m != -INFINITY) st.sum *= exp((double)st.m - (double)mx);
+        st.m = mx;
+    }
+    if (st.m != -INFINITY) {
+        float part = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (!CHECK || v + j < V) part += __builtin_amdgcn_exp2f((s4.x[j] - st.m) * kLog2eF);
+        st.sum += (double)part;
+    }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void loss_select_kernel(LossArgs p) {
+    __shared__ uint32_t s_key[kWaves * kCap];
+    __shared__ int32_t s_id[kWaves * kCap];
+    __shared__ int s_cnt[kWaves];
+    __shared__ double s_red[kWaves];
+    __shared__ float s_redf[kWaves];
+    const int row = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int V = p.V, K = p.k;
+    const float* trow = p.teacher + (size_t)row * V;
+    const float* srow = p.student + (size_t)row * V;
+    uint32_t* bk = s_key + wave * kCap;
+    int32_t* bi = s_id + wave * kCap;
+
+    StreamState st;
+    // Each pass of the workgroup covers 4 * kThreads consecutive tokens (a wave 256,
+    // a lane 4); kDepth - 1 passes of loads stay in flight while one is consumed.
+    constexpr int kStep = 4 * kThreads;
+    const int nit = (V + kStep - 1) / kStep;
+    const int v0 = wave * 256 + lane * 4;
+    F4 tr[kDepth], sr[kDepth];
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+        tr[d] = load4<VEC>(trow, v0 + d * kStep, V);
+        sr[d] = load4<VEC>(srow, v0 + d * kStep, V);
+    }
+    for (int it = 0; it < nit; it += kDepth) {
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) {
+            const int v = v0 + (it + d) * kStep;
+            if ((it + d + 1) * kStep <= V)
+                consume<false>(tr[d], sr[d], v, V, lane, bk, bi, K, st);
+            else
+                consume<true>(tr[d], sr[d], v, V, lane, bk, bi, K, st);
+            // refill the slot only once its values are consumed (the same registers)
+            tr[d] = load4<VEC>(trow, v + kDepth * kStep, V);
+            sr[d] = load4<VEC>(srow, v + kDepth * kStep, V);
+        }
+    }
+    // each wave's own k best
+    int cnt = st.cnt;
+    if (cnt > K) {
+        wave_keep<kPerWave>(bk, bi, cnt, K, lane, st.tk, st.ti);
+        cnt = K;
+    }
+    if (lane == 0) s_cnt[wave] = cnt;
+
+    // student: logsumexp from the lanes' (max, sum) pairs
+    const float m = st.m;
+    const float M = block_max(m, s_redf);
+    const double lane_part = (m == -INFINITY) ? 0.0 : st.sum * exp((double)m - (double)M);
+    const double Z = block_sum(lane_part, s_red);
+    const double lse = (double)M + log(Z);
+
+    // merge the four lists to the front of the shared buffer, then cut to k
+    int pre = 0, n = 0;
+    for (int w = 0; w < kWaves; ++w) {
+        if (w < wave) pre += s_cnt[w];
+        n += s_cnt[w];
+    }
+    constexpr int kHold = MTPV_LOSS_MAX_TOPK / 64;
+    uint32_t hk[kHold];
+    int hi[kHold];
+#pragma unroll
+    for (int e = 0; e < kHold; ++e) {
+        const int pos = e * 64 + lane;
+        hk[e] = pos < cnt ? bk[pos] : 0u;
+        hi[e] = pos < cnt ? bi[pos] : 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < kHold; ++e) {
+        const int pos = e * 64 + lane;
+        if (pos < cnt) {
+            s_key[pre + pos] = hk[e];
+            s_id[pre + pos] = hi[e];
+        }
+    }
+    __syncthreads();
+    if (wave == 0 && n > K) {
+        uint32_t mk;
+        int mi;
+        wave_keep<kPerMerge>(s_key, s_id, n, K, lane, mk, mi);
+    }
+    __syncthreads();
+
+    // rank the k kept entries (distinct under the ordering) into the area after them
+    uint32_t* rk = s_key + kWaves * MTPV_LOSS_MAX_TOPK;
+    int32_t* ri = s_id + kWaves * MTPV_LOSS_MAX_TOPK;
+    for (int a = tid; a < K; a += kThreads) {
+        const uint32_t ka = s_key[a];
+        const int ia = s_id[a];
+        int rank = 0;
+        for (int b = 0; b < K; ++b) rank += beats(s_key[b], s_id[b], ka, ia) ? 1 : 0;
+        rk[rank] = ka;
+        ri[rank] = ia;
+    }
+    __syncthreads();
+
+    // soft targets over the kept teacher logits, the student logits at them, the loss
+    const double t0 = (double)key_value(rk[0]);
+    double e_own[2] = {0.0, 0.0};
+    double z_part = 0.0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int a = tid + h * kThreads;
+        if (a < K) {
+            e_own[h] = exp((double)key_value(rk[a]) - t0);
+            z_part += e_own[h];
+        }
+    }
+    const double Zt = block_sum(z_part, s_red);
+    double dot_part = 0.0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int a = tid + h * kThreads;
+        if (a < K) {
+            const int id = ri[a];
+            const double pt = e_own[h] / Zt;
+            dot_part += pt * (double)srow[id];
+            p.index[(size_t)row * K + a] = id;
+            p.pt[(size_t)row * K + a] = pt;
+        }
+    }
+    const double dot = block_sum(dot_part, s_red);
+    if (tid == 0) {
+        p.loss[row] = (float)(lse - dot);
+        p.lse[row] = lse;
+    }
+}
+
+// grad[n, v] = scale * (q_v - pt_v), q_v = exp(s[n, v] - lse[n]), over one chunk of a
+// row; the chunk's kept tokens are first marked in LDS (their place in the kept
+// list, plus one) so every token is written once.
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void loss_grad_kernel(LossArgs p) {
+    __shared__ uint64_t slot4[kLossChunk / 4];      // 16-bit slot per token
+    __shared__ double pt[MTPV_LOSS_MAX_TOPK + 1];   // soft target per slot (slot 0: none)
+    const int row = blockIdx.x / p.chunks;
+    const int c = blockIdx.x - row * p.chunks;
+    const int v0 = c * kLossChunk;
+    for (int i = threadIdx.x; i < kLossChunk / 4; i += kThreads) slot4[i] = 0ull;
+    if (threadIdx.x == 0) pt[0] = 0.0;
+    __syncthreads();
+    uint16_t* slot = reinterpret_cast<uint16_t*>(slot4);
+    const int32_t* kept = p.index + (size_t)row * p.k;
+    const double* kept_pt = p.pt + (size_t)row * p.k;
+    for (int r = threadIdx.x; r < p.k; r += kThreads) {
+        const int id = kept[r];
+        if (id >= v0 && id < v0 + kLossChunk) {
+            slot[id - v0] = (uint16_t)(r + 1);
+            pt[r + 1] = kept_pt[r];
+        }
+    }
+    __syncthreads();
+    const double lse = p.lse[row];
+    const float* srow = p.student + (size_t)row * p.V;
+    float* grow = p.grad + (size_t)row * p.V;
+    constexpr int kU = kLossChunk / (4 * kThreads);
+    F4 sv[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) sv[u] = load4<VEC>(srow, v0 + u * 4 * kThreads + 4 * threadIdx.x, p.V);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+        const int off = u * 4 * kThreads + 4 * threadIdx.x;
+        const int v = v0 + off;
+        const uint64_t sl = slot4[off >> 2];
+        float g[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float q = expf((float)((double)sv[u].x[j] - lse));
+            const int r = (int)((sl >> (16 * j)) & 0xFFFFu);
+            g[j] = r ? (float)((double)p.scale * ((double)q - pt[r])) : p.scale * q;
+        }
+        if (VEC) {
+            if (v < p.V) *reinterpret_cast<float4*>(grow + v) = make_float4(g[0], g[1], g[2], g[3]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (v + j < p.V) grow[v + j] = g[j];
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_loss(const LossArgs& a, bool vec, hipStream_t stream) {
+    if (a.N == 0) return hipSuccess;
+    hipEvent_t t0, t1;  // the selection kernel is the timed one
+    const bool timed = timed_launch_events(&t0, &t1);
+    if (timed) {
+        const hipError_t re = hipEventRecord(t0, stream);
+        if (re != hipSuccess) return re;
+    }
+    if (vec)
+        hipLaunchKernelGGL(loss_select_kernel<true>, dim3(a.N), dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(loss_select_kernel<false>, dim3(a.N), dim3(kThreads), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess && timed) e = hipEventRecord(t1, stream);
+    if (e != hipSuccess || a.grad == nullptr) return e;
+    const unsigned int blocks = (unsigned int)((size_t)a.N * a.chunks);
+    if (vec)
+        hipLaunchKernelGGL(loss_grad_kernel<true>, dim3(blocks), dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(loss_grad_kernel<false>, dim3(blocks), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace mtpv
+
+using namespace mtpv;
+
+namespace {
+
+bool loss_aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t loss_ws_layout(int N, int k, size_t* off_pt, size_t* off_index) {
+    const size_t lse = ((size_t)N * sizeof(double) + 255) / 256 * 256;
+    const size_t pt = ((size_t)N * k * sizeof(double) + 255) / 256 * 256;
+    const size_t idx = ((size_t)N * k * sizeof(int32_t) + 255) / 256 * 256;
+    *off_pt = lse;
+    *off_index = lse + pt;
+    return lse + pt + idx;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mtpv_loss_workspace_bytes(int N, int topk) {
+    if (N < 0 || topk < 1 || topk > MTPV_LOSS_MAX_TOPK) return 0;
+    size_t a, b;
+    return loss_ws_layout(N, topk, &a, &b);
+}
+
+int mtp_draft_loss_topk(const float* teacher, const float* student, int N, int V, int topk, float grad_scale,
+                        float* loss, int32_t* topk_index, float* grad, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+    if (N < 0 || V < 1 || V > (1 << 30) || topk < 1 || topk > MTPV_LOSS_MAX_TOPK || topk > V ||
+        !std::isfinite(grad_scale))
+        return MTPV_EINVAL;
+    const size_t chunks = ((size_t)V + kLossChunk - 1) / kLossChunk;
+    if (grad != nullptr && (size_t)N * chunks > (size_t)INT_MAX) return MTPV_EINVAL;
+    if (N == 0) return MTPV_OK;
+    if (!teacher || !student || !loss) return MTPV_ENULL;
+    if (!loss_aligned(teacher, 4) || !loss_aligned(student, 4) || !loss_aligned(loss, 4) ||
+        !loss_aligned(topk_index, 4) || !loss_aligned(grad, 4))
+        return MTPV_EALIGN;
+    size_t off_pt, off_index;
+    const size_t need = loss_ws_layout(N, topk, &off_pt, &off_index);
+    if (workspace == nullptr || !loss_aligned(workspace, 256) || workspace_bytes < need) return MTPV_EWORKSPACE;
+    uint8_t* base = static_cast<uint8_t*>(workspace);
+    LossArgs a;
+    a.teacher = teacher;
+    a.student = student;
+    a.loss = loss;
+    a.index = topk_index ? topk_index : reinterpret_cast<int32_t*>(base + off_index);
+    a.pt = reinterpret_cast<double*>(base + off_pt);
+    a.lse = reinterpret_cast<double*>(base);
+    a.grad = grad;
+    a.scale = grad_scale;
+    a.N = N;
+    a.V = V;
+    a.k = topk;
+    a.chunks = (int)chunks;
+    // 16-byte loads when every row starts on a 16-byte boundary
+    const bool vec = V % 4 == 0 && loss_aligned(teacher, 16) && loss_aligned(student, 16) &&
+                     (grad == nullptr || loss_aligned(grad, 16));
+    return launch_loss(a, vec, static_cast<hipStream_t>(stream)) == hipSuccess ? MTPV_OK : MTPV_ELAUNCH;
+}
+
+}  // extern "C"

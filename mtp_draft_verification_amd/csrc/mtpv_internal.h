@@ -147,4 +147,26 @@ struct FuseArgs {
 
 hipError_t launch_fuse(const FuseArgs& args, hipStream_t stream);
 
+// While measurement is on (mtpv_timing_enable), hands out the start/stop event pair
+// to record around one launch of a call's dominant kernel and returns true.
+bool timed_launch_events(hipEvent_t* start, hipEvent_t* stop);
+
+// Top-k soft cross-entropy draft loss.
+constexpr int kLossChunk = 8192;  // tokens per workgroup of the gradient pass
+
+struct LossArgs {
+    const float* teacher;  // [N, V]
+    const float* student;  // [N, V]
+    float* loss;           // [N]
+    int32_t* index;        // [N, k]: kept tokens, best first
+    double* pt;            // [N, k]: soft targets in the same order
+    double* lse;           // [N]: logsumexp of each student row
+    float* grad;           // [N, V] or NULL
+    float scale;
+    int N, V, k;
+    int chunks;            // gradient workgroups per row
+};
+
+hipError_t launch_loss(const LossArgs& args, bool vec, hipStream_t stream);
+
 }  // namespace mtpv

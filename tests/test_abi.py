@@ -171,3 +171,35 @@ def test_fuse_call_validates_on_the_host():
     assert call(hidden=vp(A + 8)) == -2
     assert call(wsb=1024) == -3
     assert call(ws=vp(WS + 16)) == -3
+
+
+def test_loss_call_validates_on_the_host():
+    """mtp_draft_loss_topk: workspace sizing and every host-side error, without a GPU."""
+    L = mv.lib()
+    vp = ctypes.c_void_p
+    assert L.mtpv_loss_workspace_bytes(8, 256) >= 8 * 8 + 8 * 256 * (8 + 4)
+    assert L.mtpv_loss_workspace_bytes(8, 0) == 0
+    assert L.mtpv_loss_workspace_bytes(8, mv.LOSS_MAX_TOPK + 1) == 0
+    assert L.mtpv_loss_workspace_bytes(-1, 4) == 0
+    ok = dict(t=vp(A), s=vp(A), N=8, V=1000, k=256, scale=1.0, loss=vp(A), idx=None, grad=None, ws=vp(WS),
+              wsb=1 << 30)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.mtp_draft_loss_topk(a["t"], a["s"], a["N"], a["V"], a["k"], a["scale"], a["loss"], a["idx"],
+                                     a["grad"], a["ws"], a["wsb"], None)
+    assert call(N=-1) == -1
+    assert call(V=0) == -1
+    assert call(k=0) == -1
+    assert call(k=1001) == -1                       # topk > V
+    assert call(k=mv.LOSS_MAX_TOPK + 1, V=4096) == -1
+    assert call(scale=float("inf")) == -1
+    assert call(N=0, t=None, s=None, loss=None) == 0   # nothing to do
+    assert call(t=None) == -5
+    assert call(loss=None) == -5
+    assert call(s=vp(A + 2)) == -2
+    assert call(grad=vp(A + 1)) == -2
+    assert call(idx=vp(A + 2)) == -2
+    assert call(wsb=64) == -3
+    assert call(ws=vp(WS + 16)) == -3
+    assert call(ws=None) == -3
