@@ -33,7 +33,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kCap = 1248;                 // entries per wave buffer
+constexpr int kCap = 1120;                 // entries per wave buffer
 constexpr int kRoom = 256;                 // most entries one pass can add (64 lanes x 4)
 constexpr int kDepth = 4;                  // passes of loads in flight per wave
 constexpr int kPerWave = (kCap + 63) / 64; // buffer entries per lane when a wave compacts
@@ -62,70 +62,156 @@ __device__ __forceinline__ int lanes_below(unsigned long long m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-__device__ __forceinline__ int wave_max_int(int v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off));
-    return v;
+// Wave-wide inclusive prefix sum and maximum over the lanes in ascending order, with
+// DPP row shifts and row broadcasts (register-to-register, no LDS round trip).
+__device__ __forceinline__ int wave_prefix_sum(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
+    return x;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false));
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+__device__ __forceinline__ int wave_max_int(int x) {
+    x = max(x, __builtin_amdgcn_update_dpp(INT_MIN, x, 0x111, 0xF, 0xF, false));
+    x = max(x, __builtin_amdgcn_update_dpp(INT_MIN, x, 0x112, 0xF, 0xF, false));
+    x = max(x, __builtin_amdgcn_update_dpp(INT_MIN, x, 0x114, 0xF, 0xF, false));
+    x = max(x, __builtin_amdgcn_update_dpp(INT_MIN, x, 0x118, 0xF, 0xF, false));
+    x = max(x, __builtin_amdgcn_update_dpp(INT_MIN, x, 0x142, 0xA, 0xF, false));
+    x = max(x, __builtin_amdgcn_update_dpp(INT_MIN, x, 0x143, 0xC, 0xF, false));
+    return __builtin_amdgcn_readlane(x, 63);
 }
 
 // Keeps the `want` best entries (larger key, then lower index) among the first n of
 // (bk, bi), moved to positions [0, want) in no particular order, and returns the
-// worst kept entry in (tk, ti). Runs on one whole wave; n <= 64 * PER and
-// want <= n; every entry's key is above 0 (no NaN logits).
+// worst kept entry in (tk, ti). Runs on one whole wave with its own 256-bin LDS
+// histogram; n <= 64 * PER and 1 <= want <= n.
+// The want-th largest key T is found a byte at a time from the top (radix select):
+// count the entries that share the bits fixed so far by their next 8 bits, then take
+// the digit where the count from the top reaches the number still needed. The bits
+// common to all entries are fixed first (they would put every entry in one bin).
 template <int PER>
-__device__ void wave_keep(uint32_t* bk, int32_t* bi, int n, int want, int lane, uint32_t& tk, int& ti) {
-    uint32_t k[PER];
-    int id[PER];
-#pragma unroll
+__device__ void wave_keep(uint32_t* bk, int32_t* bi, int n, int want, int lane, uint32_t* hist, uint32_t& tk,
+                          int& ti) {
+    // Loops stay rolled and read the buffer from LDS each time: this runs rarely,
+    // inside the streaming loop, and kept small it leaves that loop's code compact.
+    // bits above the highest one where the largest and smallest keys differ are
+    // shared by every entry: the byte-wise search starts below them
+    uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
+#pragma nounroll
     for (int e = 0; e < PER; ++e) {
         const int pos = e * 64 + lane;
-        const bool ok = pos < n;
-        k[e] = ok ? bk[pos] : 0u;
-        id[e] = ok ? bi[pos] : INT_MAX;
+        if (pos < n) {
+            const uint32_t key = bk[pos];
+            kmax = max(kmax, key);
+            kmin = min(kmin, key);
+        }
     }
-    // the want-th largest key, decided bit by bit from the top
-    uint32_t T = 0u;
-    for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t c = T | (1u << bit);
-        int cnt = 0;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) cnt += __popcll(__ballot(k[e] >= c));
-        if (cnt >= want) T = c;
+    kmax = wave_max_u32(kmax);
+    kmin = ~wave_max_u32(~kmin);
+    const uint32_t diff = kmax ^ kmin;
+    const int top = diff ? 31 - __clz(diff) : -1;  // highest differing bit (-1: all equal)
+    uint32_t pmask = top < 0 ? 0xFFFFFFFFu : top == 31 ? 0u : ~((2u << top) - 1u);  // bits fixed so far
+    uint32_t prefix = kmax & pmask;
+    int need = want;
+#pragma nounroll
+    for (int hi = top; hi >= 0; hi -= 8) {
+        const int lo = max(hi - 7, 0);
+        const uint32_t dmask = (2u << (hi - lo)) - 1u;
+        *reinterpret_cast<uint4*>(hist + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
+#pragma nounroll
+        for (int e = 0; e < PER; ++e) {
+            const int pos = e * 64 + lane;
+            if (pos < n) {
+                const uint32_t key = bk[pos];
+                if ((key & pmask) == prefix) atomicAdd(&hist[255u - ((key >> lo) & dmask)], 1u);
+            }
+        }
+        // lane l holds bins 255-4l .. 252-4l (high digits on low lanes), so a prefix
+        // sum over the lanes counts the entries at or above each lane's lowest digit
+        const uint4 h = *reinterpret_cast<const uint4*>(hist + 4 * lane);
+        const int c = (int)(h.x + h.y + h.z + h.w);
+        const int S = wave_prefix_sum(c);
+        const unsigned long long reach = __ballot(S >= need);  // lanes L..63 (S grows with the lane)
+        const int L = __ffsll((long long)reach) - 1;
+        int above = S - c;  // entries in higher bins than this lane's four
+        int digit;
+        if (above + (int)h.x >= need) {
+            digit = 255 - 4 * lane;
+        } else if (above + (int)(h.x + h.y) >= need) {
+            digit = 254 - 4 * lane;
+            above += (int)h.x;
+        } else if (above + (int)(h.x + h.y + h.z) >= need) {
+            digit = 253 - 4 * lane;
+            above += (int)(h.x + h.y);
+        } else {
+            digit = 252 - 4 * lane;
+            above += (int)(h.x + h.y + h.z);
+        }
+        digit = __builtin_amdgcn_readlane(digit, L);
+        above = __builtin_amdgcn_readlane(above, L);
+        need -= above;
+        prefix |= (uint32_t)digit << lo;
+        pmask |= dmask << lo;
     }
-    int above = 0, ties = 0, tie_max = -1;
-#pragma unroll
+    const uint32_t T = prefix;  // need = entries of key T to keep, the lowest indices first
+    int ties = 0, tie_max = -1;
+#pragma nounroll
     for (int e = 0; e < PER; ++e) {
-        above += __popcll(__ballot(k[e] > T));
-        const bool t = k[e] == T;
+        const int pos = e * 64 + lane;
+        const bool t = pos < n && bk[pos] == T;
         ties += __popcll(__ballot(t));
-        if (t) tie_max = max(tie_max, id[e]);
+        if (t) tie_max = max(tie_max, bi[pos]);
     }
     tie_max = wave_max_int(tie_max);
-    const int r = want - above;  // entries of key T to keep: the r lowest indices
     int I = tie_max;
-    if (r < ties) {
+    if (need < ties) {
         int lo = 0, hi = tie_max;
         while (lo < hi) {
             const int mid = lo + ((hi - lo) >> 1);
             int c = 0;
-#pragma unroll
-            for (int e = 0; e < PER; ++e) c += __popcll(__ballot(k[e] == T && id[e] <= mid));
-            if (c >= r)
+#pragma nounroll
+            for (int e = 0; e < PER; ++e) {
+                const int pos = e * 64 + lane;
+                c += __popcll(__ballot(pos < n && bk[pos] == T && bi[pos] <= mid));
+            }
+            if (c >= need)
                 hi = mid;
             else
                 lo = mid + 1;
         }
         I = lo;
     }
+    // compact in place: an entry's new slot is never above its old one, and each
+    // group of 64 is read before any of it is overwritten
     int base = 0;
-#pragma unroll
+#pragma nounroll
     for (int e = 0; e < PER; ++e) {
-        const bool s = k[e] > T || (k[e] == T && id[e] <= I);
+        const int pos = e * 64 + lane;
+        uint32_t key = 0u;
+        int idx = INT_MAX;
+        if (pos < n) {
+            key = bk[pos];
+            idx = bi[pos];
+        }
+        const bool s = pos < n && (key > T || (key == T && idx <= I));
         const unsigned long long m = __ballot(s);
         if (s) {
-            const int pos = base + lanes_below(m);
-            bk[pos] = k[e];
-            bi[pos] = id[e];
+            const int to = base + lanes_below(m);
+            bk[to] = key;
+            bi[to] = idx;
         }
         base += __popcll(m);
     }
@@ -194,28 +280,33 @@ constexpr float kLog2eF = 1.44269504088896340736f;
 // the pass reaches past the row's end (tokens >= V are masked).
 template <bool CHECK>
 __device__ __forceinline__ void consume(const F4& t4, const F4& s4, int v, int V, int lane, uint32_t* bk,
-                                        int32_t* bi, int K, StreamState& st) {
-    // teacher: only a value >= the worst kept one can beat it
-    bool any = false;
+                                        int32_t* bi, uint32_t* hist, int K, StreamState& st) {
+    // teacher: with thr the value of the worst kept entry (tk, ti), a token beats it
+    // exactly when t > thr, or t == thr and its index is lower (equal floats have
+    // equal keys, -0.0 included); before the first cut thr = -inf and ti = INT_MAX
+    // admit every token
+    bool sel[4];
+    int nsel = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) any |= t4.x[j] >= st.thr;
-    if (__ballot(any)) {
+    for (int j = 0; j < 4; ++j) {
+        sel[j] = (!CHECK || v + j < V) && (t4.x[j] > st.thr || (t4.x[j] == st.thr && v + j < st.ti));
+        nsel += sel[j] ? 1 : 0;
+    }
+    if (__ballot(nsel != 0)) {
+        // slots for the lane's picks: an exclusive prefix sum over the lanes
+        const int incl = wave_prefix_sum(nsel);
+        int pos = st.cnt + incl - nsel;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const uint32_t key = order_key(t4.x[j]);
-            const bool take = (!CHECK || v + j < V) && beats(key, v + j, st.tk, st.ti);
-            const unsigned long long mk = __ballot(take);
-            if (mk) {
-                if (take) {
-                    const int pos = st.cnt + lanes_below(mk);
-                    bk[pos] = key;
-                    bi[pos] = v + j;
-                }
-                st.cnt += __popcll(mk);
+            if (sel[j]) {
+                bk[pos] = order_key(t4.x[j]);
+                bi[pos] = v + j;
+                ++pos;
             }
         }
+        st.cnt += __builtin_amdgcn_readlane(incl, 63);
         if (st.cnt > kCap - kRoom) {
-            wave_keep<kPerWave>(bk, bi, st.cnt, K, lane, st.tk, st.ti);
+            wave_keep<kPerWave>(bk, bi, st.cnt, K, lane, hist, st.tk, st.ti);
             st.cnt = K;
             st.thr = key_value(st.tk);
         }
@@ -242,6 +333,7 @@ template <bool VEC>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void loss_select_kernel(LossArgs p) {
     __shared__ uint32_t s_key[kWaves * kCap];
     __shared__ int32_t s_id[kWaves * kCap];
+    __shared__ uint4 s_hist[kWaves][64];  // a 256-bin histogram per wave
     __shared__ int s_cnt[kWaves];
     __shared__ double s_red[kWaves];
     __shared__ float s_redf[kWaves];
@@ -252,6 +344,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const float* srow = p.student + (size_t)row * V;
     uint32_t* bk = s_key + wave * kCap;
     int32_t* bi = s_id + wave * kCap;
+    uint32_t* hist = reinterpret_cast<uint32_t*>(s_hist[wave]);
 
     StreamState st;
     // Each pass of the workgroup covers 4 * kThreads consecutive tokens (a wave 256,
@@ -260,19 +353,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const int nit = (V + kStep - 1) / kStep;
     const int v0 = wave * 256 + lane * 4;
     F4 tr[kDepth], sr[kDepth];
+    // issued in slot order (the order the loop refills them), so the wait before each
+    // slot's first use counts the same on the first trip as on every later one
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) {
         tr[d] = load4<VEC>(trow, v0 + d * kStep, V);
         sr[d] = load4<VEC>(srow, v0 + d * kStep, V);
+        asm volatile("" ::: "memory");
     }
     for (int it = 0; it < nit; it += kDepth) {
 #pragma unroll
         for (int d = 0; d < kDepth; ++d) {
             const int v = v0 + (it + d) * kStep;
             if ((it + d + 1) * kStep <= V)
-                consume<false>(tr[d], sr[d], v, V, lane, bk, bi, K, st);
+                consume<false>(tr[d], sr[d], v, V, lane, bk, bi, hist, K, st);
             else
-                consume<true>(tr[d], sr[d], v, V, lane, bk, bi, K, st);
+                consume<true>(tr[d], sr[d], v, V, lane, bk, bi, hist, K, st);
             // refill the slot only once its values are consumed (the same registers)
             tr[d] = load4<VEC>(trow, v + kDepth * kStep, V);
             sr[d] = load4<VEC>(srow, v + kDepth * kStep, V);
@@ -281,7 +377,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     // each wave's own k best
     int cnt = st.cnt;
     if (cnt > K) {
-        wave_keep<kPerWave>(bk, bi, cnt, K, lane, st.tk, st.ti);
+        wave_keep<kPerWave>(bk, bi, cnt, K, lane, hist, st.tk, st.ti);
         cnt = K;
     }
     if (lane == 0) s_cnt[wave] = cnt;
@@ -321,7 +417,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     if (wave == 0 && n > K) {
         uint32_t mk;
         int mi;
-        wave_keep<kPerMerge>(s_key, s_id, n, K, lane, mk, mi);
+        wave_keep<kPerMerge>(s_key, s_id, n, K, lane, hist, mk, mi);
     }
     __syncthreads();
 
