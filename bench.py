@@ -44,30 +44,64 @@ def log(*a):
 
 
 LMHEAD_SOURCES = ("lmhead.hip", "skinny.hip", "wide.hip", "mtpv_internal.h", "plan.hip")
+LOSS_SOURCES = ("loss.hip", "mtpv_internal.h")
 
 
-def lmhead_source_hash():
-    """Hash of the sources that define the LM-head kernels and their launch plan."""
+def _source_hash(files):
     h = hashlib.sha256()
-    for f in LMHEAD_SOURCES:
+    for f in files:
         h.update(f.encode())
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(wl, mode):
-    """HBM bytes per LM-head launch from the committed counter summary, if it was
-    measured on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"lmhead_{wl.name}_{mode}_traffic.md")
+def lmhead_source_hash():
+    """Hash of the sources that define the LM-head kernels and their launch plan."""
+    return _source_hash(LMHEAD_SOURCES)
+
+
+def loss_source_hash():
+    """Hash of the sources that define the draft-loss kernels."""
+    return _source_hash(LOSS_SOURCES)
+
+
+def _recorded_bytes(name, source_hash):
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     m_bytes = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not (m_hash and m_bytes) or m_hash.group(1) != lmhead_source_hash():
+    if not (m_hash and m_bytes) or m_hash.group(1) != source_hash:
         return None
     return float(m_bytes.group(1))
+
+
+def recorded_traffic(wl, mode):
+    """HBM bytes per LM-head launch from the committed counter summary, if it was
+    measured on the current kernel source; else None."""
+    return _recorded_bytes(f"lmhead_{wl.name}_{mode}_traffic.md", lmhead_source_hash())
+
+
+def recorded_loss_traffic(workload):
+    """HBM bytes per draft-loss selection launch from the committed counter summary,
+    if it was measured on the current kernel source; else None."""
+    return _recorded_bytes(f"loss_{workload}_traffic.md", loss_source_hash())
+
+
+def calibration_copy(mib):
+    """The library's plain copy kernel on `mib` MiB, 5 launches (counter calibration)."""
+    import torch
+    import mtp_draft_verification_amd as mv
+    nbytes = mib << 20
+    src = torch.empty(nbytes, dtype=torch.uint8, device=torch.device("cuda:0"))
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(5):
+        mv.copy_bytes(dst, src, nbytes)
+    torch.cuda.synchronize()
+    log(f"calibration copy: {nbytes} bytes read and written per launch, 5 launches")
 
 
 def algorithmic(wl, mode):
@@ -227,6 +261,10 @@ def bench_loss(args):
         mv.mtp_draft_loss_topk(Td, Sd, k, loss, ws, scale, idx, grad)
 
     wall, kern = _events_time(call, args.steps, args.warmup)
+    if args.calibrate_copy_mib > 0:
+        calibration_copy(args.calibrate_copy_mib)
+    workload = f"draft_loss_N{N}_V{V}_topk{k}"
+    traffic = recorded_loss_traffic(workload)
     sel_bytes = N * V * 8 + N * 4 + N * k * 4            # teacher + student once, loss + kept ids
     call_bytes = N * V * 12 + N * 4 + N * k * 4          # ... + the gradient written once
     line = {"metric": "draft-loss rows/s (top-k soft cross-entropy, loss + gradient)",
@@ -234,10 +272,11 @@ def bench_loss(args):
             "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded N(0,1)*3 teacher, "
             "student = teacher + N(0,1))",
-            "config": {"workload": f"draft_loss_N{N}_V{V}_topk{k}", "N": N, "V": V, "topk": k, "grad": True},
+            "config": {"workload": workload, "N": N, "V": V, "topk": k, "grad": True},
             "roofline": {"bound": "hbm", "achieved": round(sel_bytes / kern / 1e9, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(sel_bytes / kern / 1e9 / HBM_PEAK_GBS, 4),
-                         "traffic": None, "kernel_us": round(kern * 1e6, 2),
+                         "traffic": None if traffic is None else round(traffic / kern / 1e9, 1),
+                         "kernel_us": round(kern * 1e6, 2),
                          "algorithmic_bytes_per_launch": sel_bytes,
                          "call_frac": round(call_bytes / wall / 1e9 / HBM_PEAK_GBS, 4)}}
     if not args.no_cpu_baseline:
@@ -352,14 +391,7 @@ def main():
         raise RuntimeError("device error word set during the benchmark")
 
     if args.calibrate_copy_mib > 0:
-        nbytes = args.calibrate_copy_mib << 20
-        src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        src.fill_(1)
-        for _ in range(5):
-            mv.copy_bytes(dst, src, nbytes)
-        torch.cuda.synchronize()
-        log(f"calibration copy: {nbytes} bytes read and written per launch, 5 launches")
+        calibration_copy(args.calibrate_copy_mib)
 
     a_host = alen[:K].cpu().numpy()
     accepted = int(a_host.sum())
