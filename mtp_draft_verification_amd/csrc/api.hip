@@ -118,6 +118,7 @@ int launch_head(const Plan& plan, const void* xt, const void* xd, const void* w,
     // every tile at the same K offset so that the tiles running together on an XCD
     // share their hidden-state and W chunks in L2.
     la.rotate = plan.kind == KIND_WIDE ? 0 : k_rotate();
+    la.ks = plan.kind == KIND_WIDE ? plan.ks : 1;
 
     std::pair<hipEvent_t, hipEvent_t>* ev = timing_slot();
     if (ev && hipEventRecord(ev->first, stream) != hipSuccess) return MTPV_EDEVICE;
@@ -340,28 +341,40 @@ int spec_verify_dual(const void* target_hidden, const void* draft_hidden, const 
 
 // Workspace of mtp_input_fuse: the projection's LM-head workspace (its error word
 // first), then the fused rows [B, 2H] bf16.
-static int fuse_plan(int B, int H, Plan* p, size_t* x_off, size_t* total) {
+// The fc projection [2H -> H] runs on the LM-head kernels with W_fc as the head. It
+// has only H output rows, so on the tiled kernel K is split in 8 slices, one per XCD
+// (the slice of the fused rows is shared in that XCD's L2, every W_fc byte is read
+// once), the H rows in tiles so that slices x tiles fill the compute units; the
+// slices' raw products land in the workspace and a fixed-order sum writes out.
+static int fuse_plan(int B, int H, Plan* p, size_t* x_off, size_t* part_off, size_t* total) {
     if (H < 8 || H > (1 << 19)) return MTPV_EINVAL;
     const int st = make_plan(MTPV_MODE_GREEDY, B, 0, 2 * H, H, MTPV_BF16, p);
     if (st != MTPV_OK) return st;
+    if (p->kind == KIND_WIDE && p->MC == 1) {
+        p->ks = 8;
+        const int s_min = (H + wide_rows() - 1) / wide_rows();
+        p->S = std::min(std::max(s_min, 256 / p->ks), (H + 15) / 16);
+        p->grid = p->S * p->ks;
+    }
     *x_off = align_up(p->total, 256);
-    *total = *x_off + align_up((size_t)B * 2 * H * 2, 256);
+    *part_off = align_up(*x_off + (size_t)B * 2 * H * 2, 256);
+    *total = *part_off + (p->ks > 1 ? align_up((size_t)p->ks * B * H * sizeof(float), 256) : 0);
     return MTPV_OK;
 }
 
 size_t mtpv_fuse_workspace_bytes(int B, int H) {
     Plan p;
-    size_t x_off, total;
-    return fuse_plan(B, H, &p, &x_off, &total) == MTPV_OK ? total : 0;
+    size_t x_off, part_off, total;
+    return fuse_plan(B, H, &p, &x_off, &part_off, &total) == MTPV_OK ? total : 0;
 }
 
 int mtp_input_fuse(const int32_t* tokens, const void* embed, const void* hidden, const void* norm_emb,
                    const void* norm_hidden, const void* W_fc, int B, int H, int V, double eps, float* out,
                    void* workspace, size_t workspace_bytes, void* stream) {
     Plan p;
-    size_t x_off, total;
+    size_t x_off, part_off, total;
     if (B < 1 || V < 1 || V > (1 << 26) || !(std::isfinite(eps) && eps >= 0.0)) return MTPV_EINVAL;
-    int st = fuse_plan(B, H, &p, &x_off, &total);
+    int st = fuse_plan(B, H, &p, &x_off, &part_off, &total);
     if (st != MTPV_OK) return st;
     if (H % 8 != 0) return MTPV_EALIGN;
     if (!tokens || !embed || !hidden || !norm_emb || !norm_hidden || !W_fc || !out) return MTPV_ENULL;
@@ -385,11 +398,14 @@ int mtp_input_fuse(const int32_t* tokens, const void* embed, const void* hidden,
     fa.eps = (float)eps;
     if (launch_fuse(fa, s) != hipSuccess) return MTPV_ELAUNCH;
     // the projection: fused rows in the place of hidden states, W_fc in the place of
-    // the head, the fp32 result through the logit output; the error word is the
-    // fusion kernel's
-    return launch_head(p, base + x_off, nullptr, W_fc, nullptr, (float)kLog2e,
-                       reinterpret_cast<Partial*>(base + p.off_partials), reinterpret_cast<float*>(base + p.off_dlogit),
-                       out, nullptr, s);
+    // the head, the fp32 result through the logit output (or the K slices' products,
+    // then their sum); the error word is the fusion kernel's
+    float* part = reinterpret_cast<float*>(base + part_off);
+    st = launch_head(p, base + x_off, nullptr, W_fc, nullptr, (float)kLog2e,
+                     reinterpret_cast<Partial*>(base + p.off_partials), reinterpret_cast<float*>(base + p.off_dlogit),
+                     p.ks > 1 ? part : out, nullptr, s);
+    if (st != MTPV_OK || p.ks == 1) return st;
+    return launch_ksum(part, out, p.ks, (size_t)B * H, s) == hipSuccess ? MTPV_OK : MTPV_ELAUNCH;
 }
 
 int spec_draft_sample(const void* draft_hidden, const void* W_lm, int B, int kd, int depth0, int H, int V,

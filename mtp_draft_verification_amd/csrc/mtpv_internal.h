@@ -55,6 +55,8 @@ struct Plan {
     int tiles;       // skinny kernel: 4-row tiles per wave
     size_t lds;      // dynamic LDS bytes of the LM-head kernel
     int grid;        // LM-head workgroups (1-D, XCD-aware ordering when MC > 1)
+    int ks;          // wide kernel: K slices (1: whole K per tile; > 1: raw partial
+                     // products per slice into the spill, summed by launch_ksum)
     int NJ;          // inverse-CDF jobs (0 in greedy mode)
     int C;           // chunks per job in the residual passes
     int ntiles;      // 64-element tiles per vocabulary row
@@ -80,7 +82,12 @@ struct LmHeadArgs {
     int32_t* err;           // cleared by the first workgroup (NULL: left alone)
     int tiles;              // skinny kernel: 4-row tiles per wave
     int rotate;             // skinny / wide kernels: rotation of the K order per wave / workgroup
+    int ks;                 // wide kernel: K slices (> 1 needs MC == 1; spill = [ks, Meff, V])
 };
+
+// out[i] = sum over s < ks of part[s * n + i], in slice order (n % 4 == 0, 16-byte
+// aligned): the K slices of a split wide-kernel launch.
+hipError_t launch_ksum(const float* part, float* out, int ks, size_t n, hipStream_t stream);
 
 hipError_t launch_lmhead(const Plan& plan, const LmHeadArgs& args, hipStream_t stream);
 hipError_t launch_skinny(const Plan& plan, const LmHeadArgs& args, hipStream_t stream);

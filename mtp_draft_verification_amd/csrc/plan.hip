@@ -46,6 +46,7 @@ int make_plan(int mode, int B, int k, int H, int V, int dtype, Plan* pl) {
     p.V = V;
     p.dtype = dtype;
     p.es = dtype == MTPV_BF16 ? 2 : 4;
+    p.ks = 1;
     if (mode == MTPV_MODE_DRAFT) {
         p.Mt = 0;
         p.Meff = B * k;

@@ -29,6 +29,8 @@
 // Accumulation is fp32 over all of H in a fixed order; no split-K, no atomics.
 #include "mtpv_internal.h"
 
+#include <algorithm>
+
 #include <climits>
 
 namespace mtpv {
@@ -146,9 +148,15 @@ __global__ __launch_bounds__(512, 1) void wide_kernel(LmHeadArgs p) {
     const int V = p.V;
     const int S = p.S;  // vocabulary tiles (= partials per position)
 
-    // workgroup -> (vocabulary tile, position chunk); the chunks of one tile share an XCD
-    int vt, mt;
-    if (p.MC == 1) {
+    // workgroup -> (vocabulary tile, position chunk); the chunks of one tile share an XCD.
+    // With K split in ks slices (MC == 1), workgroup g takes slice g % ks of tile
+    // g / ks: with ks = 8 each XCD works on one slice of K.
+    int vt, mt, ksl = 0;
+    if (p.ks > 1) {
+        vt = blockIdx.x / p.ks;
+        ksl = blockIdx.x - vt * p.ks;
+        mt = 0;
+    } else if (p.MC == 1) {
         vt = blockIdx.x;
         mt = 0;
     } else {
@@ -167,11 +175,15 @@ __global__ __launch_bounds__(512, 1) void wide_kernel(LmHeadArgs p) {
     const int v0 = min(V, 16 * (int)((long long)vt * G / S));
     const int v1 = min(V, 16 * (int)((long long)(vt + 1) * G / S));
     const int m0 = mt * BM;
-    const int nk = (H + BK - 1) / BK;
+    // K stages [kbeg, kbeg + nk) of the nk_all in H (all of them unless K is split)
+    const int nk_all = (H + BK - 1) / BK;
+    const int nk_per = (nk_all + p.ks - 1) / p.ks;
+    const int kbeg = min(nk_all, ksl * nk_per);
+    const int nk = min(nk_all, kbeg + nk_per) - kbeg;
     const size_t rowbytes = (size_t)H * 2;
     // optional rotation of the K order per vocabulary tile (the position chunks of
     // one tile share it, and so their W in L2)
-    const int kb0 = p.rotate ? (int)(((unsigned)vt * 7u) % (unsigned)nk) : 0;
+    const int kb0 = p.ks > 1 ? kbeg : p.rotate ? (int)(((unsigned)vt * 7u) % (unsigned)nk) : 0;
 
     // ------------------------------------------------------------ stage loads
     // W instruction j (j = wave * LPW_W + i) fills staged W rows RPI j .. RPI j + RPI - 1,
@@ -197,7 +209,7 @@ __global__ __launch_bounds__(512, 1) void wide_kernel(LmHeadArgs p) {
     }
     auto stage_k = [&](int kb) {
         const int kk = kb + kb0;
-        return kk >= nk ? kk - nk : kk;
+        return kk >= nk_all ? kk - nk_all : kk;
     };
     // chunks past H: W re-reads the row start, X reads sixteen zero bytes
     auto issue_w = [&](int kb) {
@@ -299,6 +311,31 @@ __global__ __launch_bounds__(512, 1) void wide_kernel(LmHeadArgs p) {
     const int vbase = v0 + vw * 64;
     const int vr = min(64, v1 - vbase);  // valid rows of this wave (may be <= 0)
     const int mrows = min(BM, p.Meff - m0);
+    if (p.ks > 1) {
+        // K split: this slice's raw products into slice ksl of [ks, Meff, V]
+        float* part = p.spill + (size_t)ksl * p.Meff * V;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int pl = mw * (BM / 2) + 16 * fm + lrow;
+            if (pl < mrows) {
+#pragma unroll
+                for (int fv = 0; fv < 4; ++fv) {
+                    const int vo = 16 * fv + 4 * lgrp;
+                    if (vo < vr) {
+                        float* dst = part + (size_t)(m0 + pl) * V + vbase + vo;
+                        if (vec_spill && vo + 3 < vr) {
+                            *(f32x4_t*)dst = acc[fv][fm];
+                        } else {
+#pragma unroll
+                            for (int t = 0; t < 4; ++t)
+                                if (vo + t < vr) dst[t] = acc[fv][fm][t];
+                        }
+                    }
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
         const int pl = mw * (BM / 2) + 16 * fm + lrow;  // position within the tile
@@ -410,6 +447,34 @@ int wide_rows() { return BV; }
 
 size_t wide_lds_bytes(int bm) {
     return bm == 256 ? WideCfg<256>::LDS : bm == 128 ? WideCfg<128>::LDS : WideCfg<64>::LDS;
+}
+
+namespace {
+
+__global__ __launch_bounds__(256) void ksum_kernel(const float4* __restrict__ part, float4* __restrict__ out, int ks,
+                                                   size_t n4) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
+        float4 a = part[i];
+        for (int s = 1; s < ks; ++s) {
+            const float4 b = part[(size_t)s * n4 + i];
+            a.x += b.x;
+            a.y += b.y;
+            a.z += b.z;
+            a.w += b.w;
+        }
+        out[i] = a;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_ksum(const float* part, float* out, int ks, size_t n, hipStream_t stream) {
+    const size_t n4 = n / 4;
+    const unsigned int blocks = (unsigned int)std::min<size_t>((n4 + 255) / 256, 2048);
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(ksum_kernel, dim3(blocks), dim3(256), 0, stream, reinterpret_cast<const float4*>(part),
+                       reinterpret_cast<float4*>(out), ks, n4);
+    return hipGetLastError();
 }
 
 hipError_t launch_wide(const Plan& plan, const LmHeadArgs& args, hipStream_t stream) {
