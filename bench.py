@@ -13,11 +13,14 @@ bf16 head, B=1 request, k=3 drafts, greedy verification. Inputs cycle through a 
 of distinct seeded steps; drafts are drawn beforehand by the library's own drafter
 call (Philox word 2) from the drafter hidden states.
 
-Prints one JSON line: verified positions/s (value), accepted tokens/s, the LM-head
-kernel's achieved HBM bandwidth against the 8 TB/s peak (kernel time from HIP events
-recorded by the library on the call's stream), the hardware-counter traffic recorded
-under profiles/ when it was taken on the current kernel source, and the CPU oracle
-timed on a bounded sample of the same workload.
+Prints one JSON line: verified positions/s (value), accepted and emitted tokens/s, the
+per-depth acceptance P(a >= d) and the accepted-length histogram, the whole call's time
+(median, p10, p90 from events on the call's stream, in a second pass over the same
+inputs after the timed loop), the LM-head kernel's
+achieved HBM bandwidth against the 8 TB/s peak (kernel time from HIP events recorded by
+the library on the call's stream), the hardware-counter traffic recorded under
+profiles/ when it was taken on the current kernel source, and the CPU oracle timed on a
+bounded sample of the same workload.
 """
 import argparse
 import hashlib
@@ -390,11 +393,24 @@ def main():
     if mv.device_error(ws) != 0:
         raise RuntimeError("device error word set during the benchmark")
 
+    # per-call time of the whole call (every kernel of it), from events on the stream the
+    # library launches on (torch's current stream), in a second pass over the same inputs
+    # so that the event records stay out of the timed loop above
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for i in range(K):
+        ev[i][0].record()
+        step(i, i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    t_call = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+
     if args.calibrate_copy_mib > 0:
         calibration_copy(args.calibrate_copy_mib)
 
     a_host = alen[:K].cpu().numpy()
     accepted = int(a_host.sum())
+    a_hist = np.bincount(a_host.ravel(), minlength=k + 1)[:k + 1]
+    pos_d = [float((a_host >= d).mean()) for d in range(1, k + 1)]
     positions = B * (k + 1) * K
     value = positions / elapsed
     alg_bytes, alg_flops = algorithmic(wl, mode)
@@ -425,6 +441,12 @@ def main():
         "accepted_tokens_per_s": round(accepted / elapsed, 2),
         "emitted_tokens_per_s": round((accepted + B * K) / elapsed, 1),
         "mean_acceptance_length": round(1 + accepted / (B * K), 4),
+        "acceptance": {"pos_d": [round(x, 5) for x in pos_d],
+                       "rate": round(float(np.mean(pos_d)), 5) if k > 0 else None,
+                       "a_hist": a_hist.tolist()},
+        "t_call_us": {"median": round(float(np.median(t_call)), 2),
+                      "p10": round(float(np.percentile(t_call, 10)), 2),
+                      "p90": round(float(np.percentile(t_call, 90)), 2)},
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
