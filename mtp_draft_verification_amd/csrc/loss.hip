@@ -37,9 +37,8 @@ constexpr int kCap = 1120;                 // entries per wave buffer
 constexpr int kRoom = 256;                 // most entries one pass can add (64 lanes x 4)
 constexpr int kDepth = 4;                  // passes of loads in flight per wave
 constexpr int kPerWave = (kCap + 63) / 64; // buffer entries per lane when a wave compacts
-constexpr int kPerMerge = kWaves * MTPV_LOSS_MAX_TOPK / 64;
 static_assert(kCap - kRoom >= MTPV_LOSS_MAX_TOPK + 256, "room between compactions");
-static_assert(kWaves * kCap >= kWaves * MTPV_LOSS_MAX_TOPK + MTPV_LOSS_MAX_TOPK, "merge and rank areas");
+static_assert(kCap % 4 == 0 && kCap >= 2 * MTPV_LOSS_MAX_TOPK, "16-byte rank reads; rank area after the kept entries");
 
 // Monotone map of an fp32 value to an unsigned key (larger value, larger key);
 // -0.0 maps to the key of +0.0.
@@ -331,8 +330,10 @@ __device__ __forceinline__ void consume(const F4& t4, const F4& s4, int v, int V
 
 template <bool VEC>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void loss_select_kernel(LossArgs p) {
-    __shared__ uint32_t s_key[kWaves * kCap];
-    __shared__ int32_t s_id[kWaves * kCap];
+    __shared__ __attribute__((aligned(16))) uint32_t s_key[kWaves * kCap];
+    __shared__ __attribute__((aligned(16))) int32_t s_id[kWaves * kCap];
+    __shared__ uint32_t s_u[8];
+    __shared__ int s_i[8];
     __shared__ uint4 s_hist[kWaves][64];  // a 256-bin histogram per wave
     __shared__ int s_cnt[kWaves];
     __shared__ double s_red[kWaves];
@@ -374,61 +375,179 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             sr[d] = load4<VEC>(srow, v + kDepth * kStep, V);
         }
     }
-    // each wave's own k best
-    int cnt = st.cnt;
-    if (cnt > K) {
-        wave_keep<kPerWave>(bk, bi, cnt, K, lane, hist, st.tk, st.ti);
-        cnt = K;
-    }
-    if (lane == 0) s_cnt[wave] = cnt;
-
-    // student: logsumexp from the lanes' (max, sum) pairs
+    // student: logsumexp from the lanes' (max, sum) pairs (the barriers in the block
+    // reductions also publish every wave's list length)
+    if (lane == 0) s_cnt[wave] = st.cnt;
     const float m = st.m;
     const float M = block_max(m, s_redf);
     const double lane_part = (m == -INFINITY) ? 0.0 : st.sum * exp((double)m - (double)M);
     const double Z = block_sum(lane_part, s_red);
     const double lse = (double)M + log(Z);
 
-    // merge the four lists to the front of the shared buffer, then cut to k
-    int pre = 0, n = 0;
-    for (int w = 0; w < kWaves; ++w) {
-        if (w < wave) pre += s_cnt[w];
-        n += s_cnt[w];
-    }
-    constexpr int kHold = MTPV_LOSS_MAX_TOPK / 64;
-    uint32_t hk[kHold];
-    int hi[kHold];
-#pragma unroll
-    for (int e = 0; e < kHold; ++e) {
-        const int pos = e * 64 + lane;
-        hk[e] = pos < cnt ? bk[pos] : 0u;
-        hi[e] = pos < cnt ? bi[pos] : 0;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < kHold; ++e) {
-        const int pos = e * 64 + lane;
-        if (pos < cnt) {
-            s_key[pre + pos] = hk[e];
-            s_id[pre + pos] = hi[e];
+    // The row's k best over the four lists (waves keep theirs where they are): a radix
+    // select by all waves over one shared histogram, then each wave cuts its own list
+    // in place. Uniform over the workgroup (every thread sees the same counts).
+    const int own = st.cnt;
+    const int n_all = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+    int kept = own;
+    if (n_all > K) {
+        uint32_t* hist0 = reinterpret_cast<uint32_t*>(s_hist);  // 256 bins
+        uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
+        for (int e = 0; e < kPerWave; ++e) {
+            const int pos = e * 64 + lane;
+            if (pos < own) {
+                const uint32_t key = bk[pos];
+                kmax = max(kmax, key);
+                kmin = min(kmin, key);
+            }
         }
+        kmax = wave_max_u32(kmax);
+        const uint32_t nkmin = wave_max_u32(~kmin);
+        if (lane == 0) {
+            s_u[wave] = kmax;
+            s_u[4 + wave] = nkmin;
+        }
+        __syncthreads();
+        kmax = max(max(s_u[0], s_u[1]), max(s_u[2], s_u[3]));
+        kmin = ~max(max(s_u[4], s_u[5]), max(s_u[6], s_u[7]));
+        const uint32_t diff = kmax ^ kmin;
+        const int top = diff ? 31 - __clz(diff) : -1;
+        uint32_t pmask = top < 0 ? 0xFFFFFFFFu : top == 31 ? 0u : ~((2u << top) - 1u);
+        uint32_t prefix = kmax & pmask;
+        int need = K;
+        for (int hi = top; hi >= 0; hi -= 8) {
+            const int lo = max(hi - 7, 0);
+            const uint32_t dmask = (2u << (hi - lo)) - 1u;
+            hist0[tid] = 0u;
+            __syncthreads();
+            for (int e = 0; e < kPerWave; ++e) {
+                const int pos = e * 64 + lane;
+                if (pos < own) {
+                    const uint32_t key = bk[pos];
+                    if ((key & pmask) == prefix) atomicAdd(&hist0[255u - ((key >> lo) & dmask)], 1u);
+                }
+            }
+            __syncthreads();
+            if (wave == 0) {
+                // lane l holds bins 255-4l .. 252-4l; a prefix sum over the lanes counts
+                // the entries at or above each lane's lowest digit
+                const uint4 h = reinterpret_cast<const uint4*>(hist0)[lane];
+                const int c = (int)(h.x + h.y + h.z + h.w);
+                const int S = wave_prefix_sum(c);
+                const int L = __ffsll((long long)__ballot(S >= need)) - 1;
+                int above = S - c;
+                int digit;
+                if (above + (int)h.x >= need) {
+                    digit = 255 - 4 * lane;
+                } else if (above + (int)(h.x + h.y) >= need) {
+                    digit = 254 - 4 * lane;
+                    above += (int)h.x;
+                } else if (above + (int)(h.x + h.y + h.z) >= need) {
+                    digit = 253 - 4 * lane;
+                    above += (int)(h.x + h.y);
+                } else {
+                    digit = 252 - 4 * lane;
+                    above += (int)(h.x + h.y + h.z);
+                }
+                if (lane == L) {
+                    s_i[0] = digit;
+                    s_i[1] = above;
+                }
+            }
+            __syncthreads();
+            need -= s_i[1];
+            prefix |= (uint32_t)s_i[0] << lo;
+            pmask |= dmask << lo;
+            __syncthreads();  // s_i is read by all before it is written again
+        }
+        const uint32_t T = prefix;  // need = entries of key T to keep, the lowest indices first
+        int ties = 0, tmax = -1;
+        for (int e = 0; e < kPerWave; ++e) {
+            const int pos = e * 64 + lane;
+            const bool t = pos < own && bk[pos] == T;
+            ties += __popcll(__ballot(t));
+            if (t) tmax = max(tmax, bi[pos]);
+        }
+        tmax = wave_max_int(tmax);
+        if (lane == 0) {
+            s_i[wave] = ties;
+            s_i[4 + wave] = tmax;
+        }
+        __syncthreads();
+        const int ties_all = s_i[0] + s_i[1] + s_i[2] + s_i[3];
+        int I = max(max(s_i[4], s_i[5]), max(s_i[6], s_i[7]));
+        __syncthreads();
+        if (need < ties_all) {
+            int lo = 0, hi = I;
+            while (lo < hi) {
+                const int mid = lo + ((hi - lo) >> 1);
+                int c = 0;
+                for (int e = 0; e < kPerWave; ++e) {
+                    const int pos = e * 64 + lane;
+                    c += __popcll(__ballot(pos < own && bk[pos] == T && bi[pos] <= mid));
+                }
+                if (lane == 0) s_i[wave] = c;
+                __syncthreads();
+                const int call = s_i[0] + s_i[1] + s_i[2] + s_i[3];
+                __syncthreads();
+                if (call >= need)
+                    hi = mid;
+                else
+                    lo = mid + 1;
+            }
+            I = lo;
+        }
+        // cut this wave's list in place: an entry's new slot is never above its old one
+        int base = 0;
+        for (int e = 0; e < kPerWave; ++e) {
+            const int pos = e * 64 + lane;
+            uint32_t key = 0u;
+            int idx = INT_MAX;
+            if (pos < own) {
+                key = bk[pos];
+                idx = bi[pos];
+            }
+            const bool keep = pos < own && (key > T || (key == T && idx <= I));
+            const unsigned long long mk = __ballot(keep);
+            if (keep) {
+                const int to = base + lanes_below(mk);
+                bk[to] = key;
+                bi[to] = idx;
+            }
+            base += __popcll(mk);
+        }
+        kept = base;
     }
     __syncthreads();
-    if (wave == 0 && n > K) {
-        uint32_t mk;
-        int mi;
-        wave_keep<kPerMerge>(s_key, s_id, n, K, lane, hist, mk, mi);
-    }
+    if (lane == 0) s_cnt[wave] = kept;
     __syncthreads();
 
-    // rank the k kept entries (distinct under the ordering) into the area after them
-    uint32_t* rk = s_key + kWaves * MTPV_LOSS_MAX_TOPK;
-    int32_t* ri = s_id + kWaves * MTPV_LOSS_MAX_TOPK;
+    // rank the k kept entries (distinct under the ordering) into the tail of the last
+    // wave's buffer (its kept entries end before k <= 512 < kCap - 512)
+    uint32_t* rk = s_key + kWaves * kCap - MTPV_LOSS_MAX_TOPK;
+    int32_t* ri = s_id + kWaves * kCap - MTPV_LOSS_MAX_TOPK;
     for (int a = tid; a < K; a += kThreads) {
-        const uint32_t ka = s_key[a];
-        const int ia = s_id[a];
+        int w = 0, j = a;
+        while (j >= s_cnt[w]) {
+            j -= s_cnt[w];
+            ++w;
+        }
+        const uint32_t ka = s_key[w * kCap + j];
+        const int ia = s_id[w * kCap + j];
         int rank = 0;
-        for (int b = 0; b < K; ++b) rank += beats(s_key[b], s_id[b], ka, ia) ? 1 : 0;
+        for (int u = 0; u < kWaves; ++u) {
+            const int cu = s_cnt[u];
+            const uint4* kq = reinterpret_cast<const uint4*>(s_key + u * kCap);
+            const int4* iq = reinterpret_cast<const int4*>(s_id + u * kCap);
+            for (int q = 0; 4 * q < cu; ++q) {
+                const uint4 kk = kq[q];
+                const int4 ii = iq[q];
+                rank += (4 * q + 0 < cu && beats(kk.x, ii.x, ka, ia)) ? 1 : 0;
+                rank += (4 * q + 1 < cu && beats(kk.y, ii.y, ka, ia)) ? 1 : 0;
+                rank += (4 * q + 2 < cu && beats(kk.z, ii.z, ka, ia)) ? 1 : 0;
+                rank += (4 * q + 3 < cu && beats(kk.w, ii.w, ka, ia)) ? 1 : 0;
+            }
+        }
         rk[rank] = ka;
         ri[rank] = ia;
     }
