@@ -20,7 +20,8 @@ inputs after the timed loop), the LM-head kernel's
 achieved HBM bandwidth against the 8 TB/s peak (kernel time from HIP events recorded by
 the library on the call's stream), the hardware-counter traffic recorded under
 profiles/ when it was taken on the current kernel source, and the CPU oracle timed on a
-bounded sample of the same workload.
+bounded sample of the same workload, which also checks the GPU's outcomes of the steps it
+shares with the timed loop (parity_vs_oracle).
 """
 import argparse
 import hashlib
@@ -125,19 +126,30 @@ def _blas_cores():
         return os.cpu_count() or 1
 
 
-def cpu_baseline(wl, mode, W_store, budget_s):
-    """The oracle as it stands, on this host's cores, over a bounded number of steps."""
+def cpu_baseline(wl, mode, W_store, budget_s, gpu=None):
+    """The oracle as it stands, on this host's cores, over a bounded number of steps.
+    gpu: the benchmark's own pooled steps (drafts and outcomes per step); for those
+    steps the oracle verifies the GPU's drafts and its outcomes are compared with the
+    GPU's under the parity tests' rule (bit-exact except decisions the oracle puts
+    within 1e-5 of a threshold, which are counted as excused)."""
     import oracle
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_util import compare_outcomes
     cores = _blas_cores()
     decode = oracle.decode_bf16 if wl.dtype == "bf16" else (lambda a: np.asarray(a, dtype=np.float64))
     W64 = decode(W_store)
     n = 0
     t_total = 0.0
     accepted = 0
+    cmp_pos = cmp_exc = cmp_fail = cmp_steps = 0
     while n < 3 or (t_total < budget_s and n < wl.steps):
         xt, xd = synth.hidden(wl, n)
         Xt, Xd = decode(xt), decode(xd)
-        drafts, _ = oracle.draft_from_hidden(Xd, W64, wl.T, wl.seed, n)   # input preparation, untimed
+        mine = gpu is not None and n < len(gpu["drafts"])
+        if mine:
+            drafts = gpu["drafts"][n]
+        else:
+            drafts, _ = oracle.draft_from_hidden(Xd, W64, wl.T, wl.seed, n)   # input preparation, untimed
         t0 = time.perf_counter()
         if mode == "greedy":
             r = oracle.verify_greedy_from_hidden(Xt, W64, drafts)
@@ -145,11 +157,21 @@ def cpu_baseline(wl, mode, W_store, budget_s):
             r = oracle.verify_sample_from_hidden(Xt, Xd, W64, drafts, wl.T, wl.seed, n)
         t_total += time.perf_counter() - t0
         accepted += int(r["a"].sum())
+        if mine:
+            npos, nexc, fails = compare_outcomes(mode, {"a": gpu["a"][n], "out": gpu["out"][n]}, r, wl.k)
+            cmp_pos += npos
+            cmp_exc += nexc
+            cmp_fail += len(fails)
+            cmp_steps += 1
         n += 1
     pos = wl.B * (wl.k + 1) * n
-    return {"value": pos / t_total, "unit": "positions/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n} steps of the same workload ({pos} verified positions), fp64 numpy, "
-                      f"{t_total:.1f} s of oracle time; accepted tokens/s {accepted / t_total:.3g}"}
+    out = {"value": pos / t_total, "unit": "positions/s", "cores": cores, "kind": "oracle",
+           "sample": f"{n} steps of the same workload ({pos} verified positions), fp64 numpy, "
+                     f"{t_total:.1f} s of oracle time; accepted tokens/s {accepted / t_total:.3g}"}
+    parity = None
+    if gpu is not None:
+        parity = {"steps": cmp_steps, "positions": cmp_pos, "excused": cmp_exc, "mismatched_requests": cmp_fail}
+    return out, parity
 
 
 def _events_time(fn, steps, warmup):
@@ -283,15 +305,27 @@ def bench_loss(args):
                          "algorithmic_bytes_per_launch": sel_bytes,
                          "call_frac": round(call_bytes / wall / 1e9 / HBM_PEAK_GBS, 4)}}
     if not args.no_cpu_baseline:
+        # the GPU's outputs of the timed call, compared row by row with the oracle's
+        loss_h, idx_h = loss.cpu().numpy(), idx.cpu().numpy()
         rows, el = 0, 0.0
+        idx_bad = loss_bad = grad_bad = 0
         while el < args.cpu_budget and rows < N:
             t0 = time.perf_counter()
-            oracle.draft_loss(T[rows:rows + 1], S[rows:rows + 1], k)
-            oracle.draft_loss_grad(T[rows:rows + 1], S[rows:rows + 1], k, scale)
+            lo, K_o = oracle.draft_loss(T[rows:rows + 1], S[rows:rows + 1], k)
+            G = oracle.draft_loss_grad(T[rows:rows + 1], S[rows:rows + 1], k, scale)
             el += time.perf_counter() - t0
+            idx_bad += int(not np.array_equal(idx_h[rows], K_o[0]))
+            loss_bad += int(abs(loss_h[rows] - lo[0]) > 2e-6 + 1e-6 * abs(lo[0]))
+            if rows < 8:  # whole gradient rows, under the parity tests' bound
+                _, _, _, lse = oracle.draft_loss_row(T[rows], S[rows], k)
+                q = np.exp(S[rows].astype(np.float64) - lse)
+                tol = scale * 4e-6 * q + 1.2e-7 * np.abs(G[0]) + 1e-30
+                grad_bad += int((np.abs(grad[rows].cpu().numpy() - G[0]) > tol).any())
             rows += 1
         line["cpu_baseline"] = {"value": round(rows / el, 2), "unit": "rows/s", "cores": _blas_cores(),
                                 "kind": "oracle", "sample": f"{rows} rows of the same call (loss + gradient)"}
+        line["parity_vs_oracle"] = {"rows": rows, "kept_id_mismatches": idx_bad, "loss_out_of_bound": loss_bad,
+                                    "gradient_rows_checked": min(rows, 8), "gradient_rows_out_of_bound": grad_bad}
     print(json.dumps(line), flush=True)
 
 
@@ -451,7 +485,10 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
-        line["cpu_baseline"] = cpu_baseline(wl, mode, W_store, args.cpu_budget)
+        nc = min(P, K)  # timed step i used pooled input i for i < P
+        gpu = {"drafts": [d.cpu().numpy() for d in d_pool[:nc]],
+               "a": alen[:nc].cpu().numpy(), "out": outt[:nc].cpu().numpy()}
+        line["cpu_baseline"], line["parity_vs_oracle"] = cpu_baseline(wl, mode, W_store, args.cpu_budget, gpu)
     print(json.dumps(line), flush=True)
 
 
