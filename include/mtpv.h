@@ -296,7 +296,8 @@ MTPV_API int mtpv_device_error(const void* workspace, int32_t* err, void* stream
 
 /*
  * Measurement hooks. While enabled, every call records a pair of HIP events on
- * its stream around the LM-head kernel (the kernel that streams W_lm). _read
+ * its stream around its dominant kernel: the LM-head kernel (the kernel that
+ * streams W_lm), or the selection kernel of mtp_draft_loss_topk. _read
  * waits for those events and returns the summed kernel time in milliseconds and
  * the number of timed launches, then clears them if reset != 0. At most 65536
  * launches are kept between reads; later ones are not timed.
