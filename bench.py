@@ -18,7 +18,8 @@ per-depth acceptance P(a >= d) and the accepted-length histogram, the whole call
 (median, p10, p90 from events on the call's stream, in a second pass over the same
 inputs after the timed loop), the LM-head kernel's
 achieved HBM bandwidth against the 8 TB/s peak (kernel time from HIP events recorded by
-the library on the call's stream), the hardware-counter traffic recorded under
+the library on the call's stream around one launch in 16 of the timed loop), the
+hardware-counter traffic recorded under
 profiles/ when it was taken on the current kernel source, and the CPU oracle timed on a
 bounded sample of the same workload, which also checks the GPU's outcomes of the steps it
 shares with the timed loop (parity_vs_oracle).
@@ -47,8 +48,9 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-LMHEAD_SOURCES = ("lmhead.hip", "skinny.hip", "wide.hip", "mtpv_internal.h", "plan.hip")
-LOSS_SOURCES = ("loss.hip", "mtpv_internal.h")
+# Paths relative to the kernel sources; the build script sets the compiler flags.
+LMHEAD_SOURCES = ("lmhead.hip", "skinny.hip", "wide.hip", "mtpv_internal.h", "plan.hip", "../build.py")
+LOSS_SOURCES = ("loss.hip", "mtpv_internal.h", "../build.py")
 
 
 def _source_hash(files):
@@ -172,6 +174,12 @@ def cpu_baseline(wl, mode, W_store, budget_s, gpu=None):
     if gpu is not None:
         parity = {"steps": cmp_steps, "positions": cmp_pos, "excused": cmp_exc, "mismatched_requests": cmp_fail}
     return out, parity
+
+
+def timing_every(steps):
+    """Time one launch in this many during a rate loop of `steps` calls (at least
+    about 32 timed launches; every launch for short loops)."""
+    return max(1, min(16, steps // 32))
 
 
 def _events_time(fn, steps, warmup):
@@ -413,7 +421,10 @@ def main():
     for i in range(args.warmup):
         step(i, K + i)
     torch.cuda.synchronize()
-    mv.timing_enable(True)
+    # Events around the LM-head kernel of one call in `every`: each event pair adds a
+    # few microseconds to its call, so the rate loop times a spread sample of calls.
+    every = timing_every(K)
+    mv.timing_enable(True, every)
     mv.timing_read(reset=True)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
@@ -423,7 +434,7 @@ def main():
     elapsed = time.perf_counter() - t_start
     kern_ms, nlaunch = mv.timing_read(reset=True)
     mv.timing_enable(False)
-    assert nlaunch == K, (nlaunch, K)
+    assert nlaunch == (K + every - 1) // every, (nlaunch, K, every)
     if mv.device_error(ws) != 0:
         raise RuntimeError("device error word set during the benchmark")
 
@@ -454,7 +465,8 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": None if traffic is None else round(traffic / kern_s / 1e9, 1),
-                "kernel_us": round(kern_s * 1e6, 2), "algorithmic_bytes_per_launch": alg_bytes,
+                "kernel_us": round(kern_s * 1e6, 2), "timed_launches": nlaunch,
+                "algorithmic_bytes_per_launch": alg_bytes,
                 "mfma_tflops": round(alg_flops / kern_s / 1e12, 2),
                 "mfma_frac": round(alg_flops / kern_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
     line = {

@@ -295,14 +295,19 @@ MTPV_API int spec_draft_sample(const void* draft_hidden, const void* W_lm, int B
 MTPV_API int mtpv_device_error(const void* workspace, int32_t* err, void* stream);
 
 /*
- * Measurement hooks. While enabled, every call records a pair of HIP events on
- * its stream around its dominant kernel: the LM-head kernel (the kernel that
- * streams W_lm), or the selection kernel of mtp_draft_loss_topk. _read
- * waits for those events and returns the summed kernel time in milliseconds and
- * the number of timed launches, then clears them if reset != 0. At most 65536
- * launches are kept between reads; later ones are not timed.
+ * Measurement hooks. mtpv_timing_enable(every) with every >= 1 makes one call in
+ * `every` (the 1st, the every+1-th, ... after enabling or a reset read) record a
+ * pair of HIP events on its stream around its dominant kernel: the LM-head kernel
+ * (the kernel that streams W_lm), or the selection kernel of mtp_draft_loss_topk.
+ * every = 1 times every call; every = 0 turns the hooks off; every < 0 returns
+ * MTPV_EINVAL. Each event pair adds a few microseconds to the call that records
+ * it, so a loop whose rate is measured at the same time times only a sample of
+ * its calls. _read waits for those events and returns the summed kernel time in
+ * milliseconds and the number of timed launches, then clears them (and restarts
+ * the count of calls) if reset != 0. At most 65536 launches are kept between
+ * reads; later ones are not timed.
  */
-MTPV_API int mtpv_timing_enable(int on);
+MTPV_API int mtpv_timing_enable(int every);
 MTPV_API int mtpv_timing_read(double* ms_total, int64_t* launches, int reset);
 
 /*

@@ -301,8 +301,9 @@ def device_error(workspace, stream=None):
     return int(err.value)
 
 
-def timing_enable(on=True):
-    _check(lib().mtpv_timing_enable(1 if on else 0), "mtpv_timing_enable")
+def timing_enable(on=True, every=1):
+    """Time one call in `every` (events around its dominant kernel) while `on`."""
+    _check(lib().mtpv_timing_enable(int(every) if on else 0), "mtpv_timing_enable")
 
 
 def timing_read(reset=True):

@@ -38,9 +38,14 @@ def hipcc():
     return exe
 
 
+# The streaming kernel's load ring lives in registers only while its step loop is
+# unrolled in full; its widest instances exceed the default size limit for that.
+EXTRA_FLAGS = {"skinny.hip": ["-mllvm", "-pragma-unroll-threshold=65536"]}
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{res.stdout}\n{res.stderr}")

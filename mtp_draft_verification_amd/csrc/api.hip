@@ -35,6 +35,8 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 struct Timing {
     std::mutex mu;
     bool on = false;
+    int every = 1;    // time one launch in `every`
+    size_t seen = 0;  // launches offered since enabling or the last reset
     std::vector<std::pair<hipEvent_t, hipEvent_t>> events;
     size_t used = 0;
 };
@@ -50,7 +52,8 @@ constexpr size_t kMaxTimed = 65536;
 std::pair<hipEvent_t, hipEvent_t>* timing_slot() {
     Timing& t = timing();
     std::lock_guard<std::mutex> lk(t.mu);
-    if (!t.on || t.used >= kMaxTimed) return nullptr;
+    if (!t.on) return nullptr;
+    if (t.seen++ % (size_t)t.every != 0 || t.used >= kMaxTimed) return nullptr;
     if (t.used == t.events.size()) {
         hipEvent_t a, b;
         if (hipEventCreate(&a) != hipSuccess) return nullptr;
@@ -429,10 +432,13 @@ int mtpv_device_error(const void* workspace, int32_t* err, void* stream) {
     return MTPV_OK;
 }
 
-int mtpv_timing_enable(int on) {
+int mtpv_timing_enable(int every) {
+    if (every < 0) return MTPV_EINVAL;
     Timing& t = timing();
     std::lock_guard<std::mutex> lk(t.mu);
-    t.on = on != 0;
+    t.on = every != 0;
+    t.every = every > 0 ? every : 1;
+    t.seen = 0;
     return MTPV_OK;
 }
 
@@ -449,7 +455,10 @@ int mtpv_timing_read(double* ms_total, int64_t* launches, int reset) {
     }
     *ms_total = total;
     *launches = (int64_t)t.used;
-    if (reset) t.used = 0;
+    if (reset) {
+        t.used = 0;
+        t.seen = 0;
+    }
     return MTPV_OK;
 }
 

@@ -101,12 +101,15 @@ __global__ __launch_bounds__(256) void skinny_kernel(LmHeadArgs p) {
     const int H = p.H;
     const int V = p.V;
     const int vb = blockIdx.x;
-    const long long ntile = (V + 3) / 4;
-    const long long nwave = 4LL * gridDim.x;
-    const long long gw = (long long)vb * 4 + wave;
-    const int t0 = (int)(gw * ntile / nwave);
-    const int T = (int)((gw + 1) * ntile / nwave) - t0;  // tiles of this wave (may be 0)
-    const int vw0 = 4 * t0;                              // first row of this wave
+    const int ntile = (V + 3) / 4;
+    const int nw = 4 * gridDim.x;
+    const int gw = vb * 4 + wave;
+    const int full = ntile / nw;          // rounds in which every wave takes a tile
+    const int rem = ntile - full * nw;    // tiles of the last, partial round
+    const int last_tile = full * nw + (int)((long long)gw * rem / nw);
+    const bool has_last = (int)((long long)(gw + 1) * rem / nw) > (int)((long long)gw * rem / nw);
+    const int T = full + (has_last ? 1 : 0);  // tiles of this wave (may be 0)
+    auto tile_row = [&](int t) { return 4 * (t < full ? t * nw + gw : last_tile); };
     const size_t rowbytes = (size_t)H * ES;
     const int nsteps = (H + KS - 1) / KS;
     const int total = max(T, 1) * nsteps;  // a wave without tiles streams nothing new
@@ -125,7 +128,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(LmHeadArgs p) {
     const int rot = p.rotate ? (int)(((unsigned)(vb * 4 + wave) * 5u) % (unsigned)nsteps) : 0;
     int lt = 0, lks = 0;
     auto next_w = [&]() -> u32x4_t {
-        const int v = min(vw0 + 4 * lt + li, V - 1);
+        const int v = min(tile_row(lt) + li, V - 1);
         int kstep = lks + rot;
         if (kstep >= nsteps) kstep -= nsteps;
         const int k = min(kstep * KS + lb * EPV, kmax);
@@ -202,7 +205,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(LmHeadArgs p) {
 
     // End of a 4-row tile: sum the 16 K-blocks, update the running statistics.
     auto finish_tile = [&](int t) {
-        const int v0 = vw0 + 4 * t;
+        const int v0 = tile_row(t);
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
             f32x4_t a = acc[g];
