@@ -63,10 +63,12 @@ int make_plan(int mode, int B, int k, int H, int V, int dtype, Plan* pl) {
         const size_t pitch = (size_t)nsteps * ks * p.es + 64;
         const size_t x_lds = (size_t)p.Meff * pitch;
         if (p.Meff <= 16 && x_lds <= (size_t)kLdsBudget) {
-            // One resident round: kCUs compute units times the workgroups their LDS
-            // holds, but no more workgroups than there are 16-row groups of tiles.
+            // One resident round: kCUs compute units times the workgroups they hold
+            // at once (by LDS, and by registers: 4 waves per SIMD up to 8 positions,
+            // 3 beyond), but no more workgroups than one tile per wave.
             p.kind = KIND_SKINNY;
-            const int per_cu = (int)std::min<size_t>(8, kLdsPerCU / std::max<size_t>(x_lds, 1024));
+            const int by_regs = p.Meff <= 8 ? 4 : 3;
+            const int per_cu = (int)std::min<size_t>(by_regs, kLdsPerCU / std::max<size_t>(x_lds, 1024));
             const int tiles = (V + 3) / 4;
             p.grid = std::max(1, std::min(kCUs * std::max(per_cu, 1), (tiles + 3) / 4));
             p.tiles = (tiles + 4 * p.grid - 1) / (4 * p.grid);

@@ -83,19 +83,38 @@ __device__ __forceinline__ Stat merge_stat(Stat a, Stat b) {
     return o;
 }
 
+// Sum over the 16 K-blocks of the 16-block 4x4x4 layout (lane = i + 4 b): rotating
+// by 4 and by 8 lanes inside each 16-lane row adds the row's four blocks and keeps
+// i = lane % 4; then row pairs and wave halves are swapped in and added. Every
+// lane ends with the same total for its i, added in the same order.
+__device__ __forceinline__ float block_sum16(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));  // row_ror:4
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));  // row_ror:8
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+}
+
 // NG groups of 4 positions, PF steps of W in flight per wave. The grid is sized
-// to what the GPU holds at once (every workgroup resident, no second round) and
-// the ceil(V / 4) row tiles are split as evenly as possible over all its waves:
-// wave w owns tiles [w * nt / nw, (w + 1) * nt / nw). A workgroup's rows are
-// contiguous and it writes one partial per position.
+// to what the GPU holds at once (every workgroup resident, no second round). The
+// ceil(V / 4) row tiles are dealt to the waves round by round: in round r wave w
+// takes tile r * n + w (n waves in the grid), so at any moment all waves stream
+// from one window of consecutive tiles; the tiles of the last, partial round are
+// spread evenly over the waves. Each workgroup writes one partial per position.
+//
+// A step's load address is a wave-uniform base (the tile's first row and the K
+// step, in scalar registers) plus a per-lane offset that changes only between
+// tiles, so the step loop spends no vector instructions on W addresses.
 template <int ES, int NG, int PF>
 __global__ __launch_bounds__(256) void skinny_kernel(LmHeadArgs p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     constexpr int EPV = Mma4<ES>::EPV;
-    constexpr int KS = 16 * EPV;  // hidden elements per step (256 bytes of a row)
+    constexpr int KS = 16 * EPV;  // hidden elements per step
+    constexpr int SB = KS * ES;   // bytes of a row per step (256)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 3;   // A: row within the tile; B / D: position within the group
     const int lb = lane >> 2;  // block: 16-byte segment of the step
     const int H = p.H;
@@ -110,42 +129,69 @@ __global__ __launch_bounds__(256) void skinny_kernel(LmHeadArgs p) {
     const bool has_last = (int)((long long)(gw + 1) * rem / nw) > (int)((long long)gw * rem / nw);
     const int T = full + (has_last ? 1 : 0);  // tiles of this wave (may be 0)
     auto tile_row = [&](int t) { return 4 * (t < full ? t * nw + gw : last_tile); };
-    const size_t rowbytes = (size_t)H * ES;
+    const int rowbytes = H * ES;  // < 64 KB: the staged rows fit the LDS budget
     const int nsteps = (H + KS - 1) / KS;
     const int total = max(T, 1) * nsteps;  // a wave without tiles streams nothing new
     const int mrows = p.Meff;  // all positions fit one workgroup here
-    const int pitch = nsteps * KS * ES + 64;
+    const int pitch = nsteps * SB + 64;
 
     if (vb == 0 && tid == 0 && p.err != nullptr) *p.err = 0;
 
-    // Address of this lane's 16 bytes for the next step to load; steps advance
-    // through K of the current tile, then on to the next tile. Past the last step
-    // the address stays on the last step (a re-read, no new HBM traffic).
-    // Each wave walks K starting at its own rotation `rot` (any order of K gives
-    // the same dot products): waves whose rows sit at power-of-two strides would
-    // otherwise hit the same HBM channels at the same moment.
-    const int kmax = H - EPV;
-    const int rot = p.rotate ? (int)(((unsigned)(vb * 4 + wave) * 5u) % (unsigned)nsteps) : 0;
+    // Steps advance through K of the current tile, then on to the next tile; past
+    // the last step the address stays on the last step (a re-read, no new HBM
+    // traffic). Each wave walks K starting at its own rotation `rot` (any order of K
+    // gives the same dot products): waves whose rows sit at power-of-two strides
+    // would otherwise hit the same HBM channels at the same moment. Rows past V
+    // re-read row V - 1; in the last step of a row that is not a whole number of
+    // steps long, segments past H re-read the row's last 16 bytes.
+    const int rot = p.rotate ? (int)(((unsigned)gw * 5u) % (unsigned)nsteps) : 0;
+    const bool ragged = nsteps * KS != H;
+    const unsigned seg = (unsigned)(lb * 16);
+    const unsigned seg_last = (unsigned)min(lb * 16, rowbytes - 16 - (nsteps - 1) * SB);
+    auto row_off = [&](int row0) { return (unsigned)(min(row0 + li, V - 1) - row0) * (unsigned)rowbytes; };
     int lt = 0, lks = 0;
+    int lrow0 = tile_row(0);
+    unsigned loff = row_off(lrow0);
     auto next_w = [&]() -> u32x4_t {
-        const int v = min(tile_row(lt) + li, V - 1);
         int kstep = lks + rot;
         if (kstep >= nsteps) kstep -= nsteps;
-        const int k = min(kstep * KS + lb * EPV, kmax);
-        const u32x4_t r = load_w(p.w + (size_t)v * rowbytes + (size_t)k * ES);
+        const uint8_t* base = p.w + (size_t)lrow0 * rowbytes + (size_t)kstep * SB;  // wave-uniform
+        const unsigned off = loff + ((ragged && kstep == nsteps - 1) ? seg_last : seg);
+        const u32x4_t r = load_w(base + off);
         if (lks + 1 < nsteps) {
             ++lks;
         } else if (lt + 1 < T) {
             lks = 0;
             ++lt;
+            lrow0 = tile_row(lt);
+            loff = row_off(lrow0);
         }
         return r;
     };
 
+    // The ring is filled unconditionally: a wave without tiles (T = 0) re-reads its
+    // would-be first tile, which lies inside W (tile_row(0) < 4 * ntile).
     u32x4_t wb[PF];
-    if (T > 0) {
 #pragma unroll
-        for (int i = 0; i < PF; ++i) wb[i] = next_w();
+    for (int i = 0; i < PF; ++i) wb[i] = next_w();
+
+    // per-lane position bookkeeping: position m = 4g + li (read before the staging
+    // below, whose wait covers these loads too)
+    int dtok[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        const int m = 4 * g + li;
+        int d = -1;
+        if (m < mrows && p.drafts != nullptr) {
+            if (m < p.Mt) {
+                const int b = m / (p.k + 1);
+                const int j = m - b * (p.k + 1);
+                d = (j < p.k) ? p.drafts[b * p.k + j] : -1;
+            } else {
+                d = p.drafts[m - p.Mt];
+            }
+        }
+        dtok[g] = d;
     }
 
     // Stage all positions' hidden states, zero-filled to nsteps * KS elements.
@@ -163,24 +209,12 @@ __global__ __launch_bounds__(256) void skinny_kernel(LmHeadArgs p) {
             *(u32x4_t*)(smem + r * pitch + c * 16) = val;
         }
     }
+    // Every load issued so far (the ring, the draft ids, the staging) is complete
+    // here in practice: the staging waits for its own loads, which were issued last.
+    // Saying so explicitly keeps the compiler from waiting for the draft ids inside
+    // the step loop, where that wait would drain the ring.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt at their maxima
 
-    // per-lane position bookkeeping: position m = 4g + li
-    int dtok[NG];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-        const int m = 4 * g + li;
-        int d = -1;
-        if (m < mrows && p.drafts != nullptr) {
-            if (m < p.Mt) {
-                const int b = m / (p.k + 1);
-                const int j = m - b * (p.k + 1);
-                d = (j < p.k) ? p.drafts[b * p.k + j] : -1;
-            } else {
-                d = p.drafts[m - p.Mt];
-            }
-        }
-        dtok[g] = d;
-    }
     const float ninf = -__builtin_inff();
     Stat st[NG];
 #pragma unroll
@@ -192,13 +226,18 @@ __global__ __launch_bounds__(256) void skinny_kernel(LmHeadArgs p) {
 
     const float c2 = p.c2;
     const bool vec_spill = (V & 3) == 0;
+    // This lane's B fragment at K step 0, per group. A lane of a missing position
+    // (past the last one in a partial group of 4) reads the last position's row: the
+    // MFMA keeps B's columns apart, so that column's logits are computed and ignored.
+    unsigned xoff[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) xoff[g] = (unsigned)(min(4 * g + li, mrows - 1) * pitch) + seg;
 
     auto consume = [&](const u32x4_t& w, int ks) {
+        const uint8_t* xs = smem + ks * SB;
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
-            const int m = 4 * g + li;
-            const u32x4_t x = (m < mrows) ? *(const u32x4_t*)(smem + m * pitch + (ks * KS + lb * EPV) * ES)
-                                          : u32x4_t{0u, 0u, 0u, 0u};
+            const u32x4_t x = *(const u32x4_t*)(xs + xoff[g]);
             acc[g] = Mma4<ES>::run(w, x, acc[g]);
         }
     };
@@ -208,12 +247,9 @@ __global__ __launch_bounds__(256) void skinny_kernel(LmHeadArgs p) {
         const int v0 = tile_row(t);
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
-            f32x4_t a = acc[g];
+            f32x4_t a;
 #pragma unroll
-            for (int off = 4; off < 64; off <<= 1) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) a[e] += __shfl_xor(a[e], off);
-            }
+            for (int e = 0; e < 4; ++e) a[e] = block_sum16(acc[g][e]);
             acc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             const int m = 4 * g + li;
             float tx = ninf;
@@ -260,31 +296,23 @@ __global__ __launch_bounds__(256) void skinny_kernel(LmHeadArgs p) {
     };
 
     // ks counts steps within the tile; kr is the K step they map to after rotation.
+    // One loop covers every step: the steps of the last batch past `work` consume
+    // nothing, and their loads (re-reads of the last step) are never waited for.
     int ks = 0, kr = rot, t = 0;
-    int s = 0;
     const int work = T > 0 ? total : 0;
-    for (; s + PF <= work; s += PF) {
+    for (int s = 0; s < work; s += PF) {
 #pragma unroll
         for (int i = 0; i < PF; ++i) {
-            consume(wb[i], kr);
+            const bool live = s + i < work;  // wave-uniform
+            if (live) consume(wb[i], kr);
             wb[i] = next_w();
-            if (++kr == nsteps) kr = 0;
-            if (++ks == nsteps) {
-                finish_tile(t);
-                ks = 0;
-                ++t;
-            }
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < PF; ++i) {
-        if (s + i < work) {
-            consume(wb[i], kr);
-            if (++kr == nsteps) kr = 0;
-            if (++ks == nsteps) {
-                finish_tile(t);
-                ks = 0;
-                ++t;
+            if (live) {
+                if (++kr == nsteps) kr = 0;
+                if (++ks == nsteps) {
+                    finish_tile(t);
+                    ks = 0;
+                    ++t;
+                }
             }
         }
     }
