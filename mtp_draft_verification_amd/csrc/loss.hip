@@ -10,10 +10,12 @@
 //
 // Selection kernel: one workgroup (4 waves) per row streams the teacher row and the
 // student row once with 16-byte loads. Each wave keeps, in LDS, the entries of its
-// share that beat a running threshold (the smallest entry it has kept); when its
-// buffer nears full it keeps only its k best (a bitwise search for the k-th key over
-// registers, ties by index) and raises the threshold; a plain float compare against
-// the threshold's value screens each token first. The student side keeps a per-lane
+// share that beat a running threshold; when its buffer nears full it cuts it to about
+// its k best (a radix search for the k-th key, stopped early once the cut is within
+// a few entries of k) and raises the threshold, and publishes a bound under which
+// fewer than k / 4 of its entries lie, so that the four waves together screen with
+// about the k-th best of all their tokens; a plain float compare against the
+// threshold's value screens each token first. The student side keeps a per-lane
 // running maximum and an fp64 sum of exp(s - max) (hardware exp2 of the scaled
 // difference, summed in fp32 per 4 tokens). At the end the four
 // waves' lists are merged and cut to k, ranked, and the soft targets, the gathered
@@ -37,7 +39,9 @@ constexpr int kCap = 1120;                 // entries per wave buffer
 constexpr int kRoom = 256;                 // most entries one pass can add (64 lanes x 4)
 constexpr int kDepth = 4;                  // passes of loads in flight per wave
 constexpr int kPerWave = (kCap + 63) / 64; // buffer entries per lane when a wave compacts
-static_assert(kCap - kRoom >= MTPV_LOSS_MAX_TOPK + 256, "room between compactions");
+constexpr int kSlack = 64;                 // a cut may keep this many entries beyond k
+constexpr int kPerKept = (MTPV_LOSS_MAX_TOPK + kSlack + 63) / 64;  // entries per lane after a cut
+static_assert(kCap - kRoom >= MTPV_LOSS_MAX_TOPK + kSlack + 256, "room between compactions");
 static_assert(kCap % 4 == 0 && kCap >= 2 * MTPV_LOSS_MAX_TOPK, "16-byte rank reads; rank area after the kept entries");
 
 // Monotone map of an fp32 value to an unsigned key (larger value, larger key);
@@ -93,21 +97,21 @@ __device__ __forceinline__ int wave_max_int(int x) {
     return __builtin_amdgcn_readlane(x, 63);
 }
 
-// Keeps the `want` best entries (larger key, then lower index) among the first n of
-// (bk, bi), moved to positions [0, want) in no particular order, and returns the
-// worst kept entry in (tk, ti). Runs on one whole wave with its own 256-bin LDS
-// histogram; n <= 64 * PER and 1 <= want <= n.
-// The want-th largest key T is found a byte at a time from the top (radix select):
-// count the entries that share the bits fixed so far by their next 8 bits, then take
-// the digit where the count from the top reaches the number still needed. The bits
-// common to all entries are fixed first (they would put every entry in one bin).
+// Radix search over the first n keys of bk for a bound T with at least `want` keys
+// >= T (1 <= want <= n), one byte at a time from the top: count the keys that share
+// the bits fixed so far by their next 8 bits, then take the digit where the count
+// from the top reaches the number still needed. The bits common to all keys are
+// fixed first (they would put every key in one bin). The search stops when every
+// bit is fixed (exact = true: T is the want-th largest key and `need` keys equal to
+// T are still needed) or when the chosen bin holds at most `slack` keys more than
+// are still needed (exact = false: T is the bin's lowest key, bits below zero, and
+// at most want + slack keys are >= T). Runs on one whole wave with its own 256-bin
+// LDS histogram; n <= 64 * PER.
 template <int PER>
-__device__ void wave_keep(uint32_t* bk, int32_t* bi, int n, int want, int lane, uint32_t* hist, uint32_t& tk,
-                          int& ti) {
+__device__ uint32_t radix_bound(const uint32_t* bk, int n, int want, int slack, int lane, uint32_t* hist, int& need,
+                                bool& exact) {
     // Loops stay rolled and read the buffer from LDS each time: this runs rarely,
     // inside the streaming loop, and kept small it leaves that loop's code compact.
-    // bits above the highest one where the largest and smallest keys differ are
-    // shared by every entry: the byte-wise search starts below them
     uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
 #pragma nounroll
     for (int e = 0; e < PER; ++e) {
@@ -124,7 +128,8 @@ __device__ void wave_keep(uint32_t* bk, int32_t* bi, int n, int want, int lane, 
     const int top = diff ? 31 - __clz(diff) : -1;  // highest differing bit (-1: all equal)
     uint32_t pmask = top < 0 ? 0xFFFFFFFFu : top == 31 ? 0u : ~((2u << top) - 1u);  // bits fixed so far
     uint32_t prefix = kmax & pmask;
-    int need = want;
+    need = want;
+    exact = true;
 #pragma nounroll
     for (int hi = top; hi >= 0; hi -= 8) {
         const int lo = max(hi - 7, 0);
@@ -146,52 +151,79 @@ __device__ void wave_keep(uint32_t* bk, int32_t* bi, int n, int want, int lane, 
         const unsigned long long reach = __ballot(S >= need);  // lanes L..63 (S grows with the lane)
         const int L = __ffsll((long long)reach) - 1;
         int above = S - c;  // entries in higher bins than this lane's four
-        int digit;
+        int digit, inbin;
         if (above + (int)h.x >= need) {
             digit = 255 - 4 * lane;
+            inbin = (int)h.x;
         } else if (above + (int)(h.x + h.y) >= need) {
             digit = 254 - 4 * lane;
             above += (int)h.x;
+            inbin = (int)h.y;
         } else if (above + (int)(h.x + h.y + h.z) >= need) {
             digit = 253 - 4 * lane;
             above += (int)(h.x + h.y);
+            inbin = (int)h.z;
         } else {
             digit = 252 - 4 * lane;
             above += (int)(h.x + h.y + h.z);
+            inbin = (int)h.w;
         }
         digit = __builtin_amdgcn_readlane(digit, L);
         above = __builtin_amdgcn_readlane(above, L);
+        inbin = __builtin_amdgcn_readlane(inbin, L);
         need -= above;
         prefix |= (uint32_t)digit << lo;
         pmask |= dmask << lo;
-    }
-    const uint32_t T = prefix;  // need = entries of key T to keep, the lowest indices first
-    int ties = 0, tie_max = -1;
-#pragma nounroll
-    for (int e = 0; e < PER; ++e) {
-        const int pos = e * 64 + lane;
-        const bool t = pos < n && bk[pos] == T;
-        ties += __popcll(__ballot(t));
-        if (t) tie_max = max(tie_max, bi[pos]);
-    }
-    tie_max = wave_max_int(tie_max);
-    int I = tie_max;
-    if (need < ties) {
-        int lo = 0, hi = tie_max;
-        while (lo < hi) {
-            const int mid = lo + ((hi - lo) >> 1);
-            int c = 0;
-#pragma nounroll
-            for (int e = 0; e < PER; ++e) {
-                const int pos = e * 64 + lane;
-                c += __popcll(__ballot(pos < n && bk[pos] == T && bi[pos] <= mid));
-            }
-            if (c >= need)
-                hi = mid;
-            else
-                lo = mid + 1;
+        if (lo > 0 && inbin - need <= slack) {
+            exact = false;
+            break;
         }
-        I = lo;
+    }
+    return prefix;
+}
+
+// Keeps at least the `want` best entries (larger key, then lower index) among the
+// first n of (bk, bi), moved to the front in no particular order, and returns how
+// many were kept. The bound found by radix_bound decides: exact, the want best are
+// kept and (tk, ti) is the worst of them; otherwise every entry of key >= T is kept
+// (at most want + slack) and (tk, ti) = (T, INT_MAX), which every key >= T beats.
+// Either way at least `want` kept entries beat or equal (tk, ti), so no entry below
+// it can be among the row's k best.
+template <int PER>
+__device__ int wave_keep(uint32_t* bk, int32_t* bi, int n, int want, int slack, int lane, uint32_t* hist,
+                         uint32_t& tk, int& ti) {
+    int need;
+    bool exact;
+    const uint32_t T = radix_bound<PER>(bk, n, want, slack, lane, hist, need, exact);
+    int I = INT_MAX;
+    if (exact) {  // need = entries of key T to keep, the lowest indices first
+        int ties = 0, tie_max = -1;
+#pragma nounroll
+        for (int e = 0; e < PER; ++e) {
+            const int pos = e * 64 + lane;
+            const bool t = pos < n && bk[pos] == T;
+            ties += __popcll(__ballot(t));
+            if (t) tie_max = max(tie_max, bi[pos]);
+        }
+        tie_max = wave_max_int(tie_max);
+        I = tie_max;
+        if (need < ties) {
+            int lo = 0, hi = tie_max;
+            while (lo < hi) {
+                const int mid = lo + ((hi - lo) >> 1);
+                int c = 0;
+#pragma nounroll
+                for (int e = 0; e < PER; ++e) {
+                    const int pos = e * 64 + lane;
+                    c += __popcll(__ballot(pos < n && bk[pos] == T && bi[pos] <= mid));
+                }
+                if (c >= need)
+                    hi = mid;
+                else
+                    lo = mid + 1;
+            }
+            I = lo;
+        }
     }
     // compact in place: an entry's new slot is never above its old one, and each
     // group of 64 is read before any of it is overwritten
@@ -216,6 +248,7 @@ __device__ void wave_keep(uint32_t* bk, int32_t* bi, int n, int want, int lane, 
     }
     tk = T;
     ti = I;
+    return base;
 }
 
 __device__ __forceinline__ double block_sum(double v, double* sh) {
@@ -277,10 +310,31 @@ constexpr float kLog2eF = 1.44269504088896340736f;
 
 // One pass of a wave: 4 teacher and 4 student values per lane from token v. CHECK:
 // the pass reaches past the row's end (tokens >= V are masked).
+//
+// The threshold (tk, ti) a token must beat is the stronger of this wave's own (the
+// worst entry its last cut kept) and a bound shared by the four waves: after each
+// cut a wave publishes a key q_w below which fewer than ceil(k / 4) of its kept
+// entries lie, so the four lists hold at least k entries of key >= min_w q_w and no
+// token below that minimum can be among the row's k best. It rises as soon as every
+// wave has cut once, to about the k-th best of all four waves' tokens so far, where
+// a wave's own threshold only reflects its quarter of them.
 template <bool CHECK>
 __device__ __forceinline__ void consume(const F4& t4, const F4& s4, int v, int V, int lane, uint32_t* bk,
-                                        int32_t* bi, uint32_t* hist, int K, StreamState& st) {
-    // teacher: with thr the value of the worst kept entry (tk, ti), a token beats it
+                                        int32_t* bi, uint32_t* hist, uint32_t* sq, int wave, int K,
+                                        StreamState& st) {
+    {
+        // relaxed workgroup-scope loads: fresh each pass, with no wait on the ring
+        uint32_t q[kWaves];
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) q[w] = __hip_atomic_load(sq + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        const uint32_t qmin = min(min(q[0], q[1]), min(q[2], q[3]));
+        if (qmin > st.tk) {
+            st.tk = qmin;
+            st.ti = INT_MAX;
+            st.thr = key_value(qmin);
+        }
+    }
+    // teacher: with thr the value of the threshold key tk, a token beats (tk, ti)
     // exactly when t > thr, or t == thr and its index is lower (equal floats have
     // equal keys, -0.0 included); before the first cut thr = -inf and ti = INT_MAX
     // admit every token
@@ -305,9 +359,13 @@ __device__ __forceinline__ void consume(const F4& t4, const F4& s4, int v, int V
         }
         st.cnt += __builtin_amdgcn_readlane(incl, 63);
         if (st.cnt > kCap - kRoom) {
-            wave_keep<kPerWave>(bk, bi, st.cnt, K, lane, hist, st.tk, st.ti);
-            st.cnt = K;
+            st.cnt = wave_keep<kPerWave>(bk, bi, st.cnt, K, kSlack, lane, hist, st.tk, st.ti);
             st.thr = key_value(st.tk);
+            int need;
+            bool exact;
+            const uint32_t q = radix_bound<kPerKept>(bk, st.cnt, (K + 3) / 4, kSlack, lane, hist, need, exact);
+            if (lane == 0)
+                __hip_atomic_store(sq + wave, max(sq[wave], q), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
     }
     // student: running maximum, then exp2 of the scaled differences (<= 0)
@@ -338,6 +396,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     __shared__ int s_cnt[kWaves];
     __shared__ double s_red[kWaves];
     __shared__ float s_redf[kWaves];
+    __shared__ uint32_t s_q[kWaves];  // the waves' shared bounds (0: none yet)
     const int row = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int V = p.V, K = p.k;
@@ -348,6 +407,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     uint32_t* hist = reinterpret_cast<uint32_t*>(s_hist[wave]);
 
     StreamState st;
+    if (tid < kWaves) s_q[tid] = 0u;
+    __syncthreads();  // before any load is in flight (a barrier would wait for them)
     // Each pass of the workgroup covers 4 * kThreads consecutive tokens (a wave 256,
     // a lane 4); kDepth - 1 passes of loads stay in flight while one is consumed.
     constexpr int kStep = 4 * kThreads;
@@ -367,9 +428,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         for (int d = 0; d < kDepth; ++d) {
             const int v = v0 + (it + d) * kStep;
             if ((it + d + 1) * kStep <= V)
-                consume<false>(tr[d], sr[d], v, V, lane, bk, bi, hist, K, st);
+                consume<false>(tr[d], sr[d], v, V, lane, bk, bi, hist, s_q, wave, K, st);
             else
-                consume<true>(tr[d], sr[d], v, V, lane, bk, bi, hist, K, st);
+                consume<true>(tr[d], sr[d], v, V, lane, bk, bi, hist, s_q, wave, K, st);
             // refill the slot only once its values are consumed (the same registers)
             tr[d] = load4<VEC>(trow, v + kDepth * kStep, V);
             sr[d] = load4<VEC>(srow, v + kDepth * kStep, V);
@@ -523,33 +584,39 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     __syncthreads();
 
     // rank the k kept entries (distinct under the ordering) into the tail of the last
-    // wave's buffer (its kept entries end before k <= 512 < kCap - 512)
+    // wave's buffer (its kept entries end before k <= 512 < kCap - 512). Each entry is
+    // first packed as key * 2^32 + (2^32 - 1 - index) into the free histogram area
+    // (512 slots; the slots up to a multiple of 4 past k hold 0, which beats nothing):
+    // one 64-bit compare then orders two entries, larger key first, lower index first.
     uint32_t* rk = s_key + kWaves * kCap - MTPV_LOSS_MAX_TOPK;
     int32_t* ri = s_id + kWaves * kCap - MTPV_LOSS_MAX_TOPK;
-    for (int a = tid; a < K; a += kThreads) {
-        int w = 0, j = a;
-        while (j >= s_cnt[w]) {
-            j -= s_cnt[w];
-            ++w;
-        }
-        const uint32_t ka = s_key[w * kCap + j];
-        const int ia = s_id[w * kCap + j];
-        int rank = 0;
-        for (int u = 0; u < kWaves; ++u) {
-            const int cu = s_cnt[u];
-            const uint4* kq = reinterpret_cast<const uint4*>(s_key + u * kCap);
-            const int4* iq = reinterpret_cast<const int4*>(s_id + u * kCap);
-            for (int q = 0; 4 * q < cu; ++q) {
-                const uint4 kk = kq[q];
-                const int4 ii = iq[q];
-                rank += (4 * q + 0 < cu && beats(kk.x, ii.x, ka, ia)) ? 1 : 0;
-                rank += (4 * q + 1 < cu && beats(kk.y, ii.y, ka, ia)) ? 1 : 0;
-                rank += (4 * q + 2 < cu && beats(kk.z, ii.z, ka, ia)) ? 1 : 0;
-                rank += (4 * q + 3 < cu && beats(kk.w, ii.w, ka, ia)) ? 1 : 0;
+    uint64_t* comp = reinterpret_cast<uint64_t*>(s_hist);
+    static_assert(sizeof(s_hist) >= MTPV_LOSS_MAX_TOPK * sizeof(uint64_t), "packed entries fit the histograms");
+    const int k4 = (K + 3) & ~3;
+    for (int a = tid; a < k4; a += kThreads) {
+        uint64_t c = 0u;
+        if (a < K) {
+            int w = 0, j = a;
+            while (j >= s_cnt[w]) {
+                j -= s_cnt[w];
+                ++w;
             }
+            c = ((uint64_t)s_key[w * kCap + j] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)s_id[w * kCap + j]);
         }
-        rk[rank] = ka;
-        ri[rank] = ia;
+        comp[a] = c;
+    }
+    __syncthreads();
+    for (int a = tid; a < K; a += kThreads) {
+        const uint64_t ca = comp[a];
+        int rank = 0;
+        const ulonglong2* cq = reinterpret_cast<const ulonglong2*>(comp);
+        for (int q = 0; q < k4 / 2; ++q) {
+            const ulonglong2 cc = cq[q];
+            rank += (cc.x > ca) ? 1 : 0;
+            rank += (cc.y > ca) ? 1 : 0;
+        }
+        rk[rank] = (uint32_t)(ca >> 32);
+        ri[rank] = (int32_t)(0xFFFFFFFFu - (uint32_t)ca);
     }
     __syncthreads();
 
