@@ -30,6 +30,7 @@
 #include "mtpv_internal.h"
 
 #include <algorithm>
+#include <type_traits>
 
 #include <climits>
 
@@ -259,48 +260,64 @@ __global__ __launch_bounds__(512, 1) void wide_kernel(LmHeadArgs p) {
     // buffers take the loads of later stages, and K-step 0 of stage kb + 1 is read
     // before K-step 1's MFMAs: the MFMAs already issued cover the barrier, the load
     // issue and the LDS latency.
-    auto read_frags = [&](int kb, int s, u32x4_t (&a)[4], u32x4_t (&b)[FM]) {
-        const uint8_t* wbase = wring + (kb % NSW) * Cfg::WSTAGE + (vw * 64) * ROWB;
-        const uint8_t* xbase = xring + (kb % NSX) * Cfg::XSTAGE + (mw * (BM / 2)) * ROWB;
-        const int fo = s == 0 ? frag_off0 : frag_off1;
+    // The stage loop for NL live position fragments of this wave: the fragments past
+    // the last position hold padding whose products would be discarded, so their X
+    // fragments are not read and their MFMAs not issued (the accumulators stay 0).
+    auto stage_loop = [&](auto nl_tag) {
+        constexpr int NL = decltype(nl_tag)::value;
+        auto read_frags = [&](int kb, int s, u32x4_t (&a)[4], u32x4_t (&b)[NL]) {
+            const uint8_t* wbase = wring + (kb % NSW) * Cfg::WSTAGE + (vw * 64) * ROWB;
+            const uint8_t* xbase = xring + (kb % NSX) * Cfg::XSTAGE + (mw * (BM / 2)) * ROWB;
+            const int fo = s == 0 ? frag_off0 : frag_off1;
 #pragma unroll
-        for (int fv = 0; fv < 4; ++fv) a[fv] = *(const u32x4_t*)(wbase + fv * 16 * ROWB + fo);
+            for (int fv = 0; fv < 4; ++fv) a[fv] = *(const u32x4_t*)(wbase + fv * 16 * ROWB + fo);
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) b[fm] = *(const u32x4_t*)(xbase + fm * 16 * ROWB + fo);
-    };
-    auto mma = [&](const u32x4_t (&a)[4], const u32x4_t (&b)[FM]) {
+            for (int fm = 0; fm < NL; ++fm) b[fm] = *(const u32x4_t*)(xbase + fm * 16 * ROWB + fo);
+        };
+        auto mma = [&](const u32x4_t (&a)[4], const u32x4_t (&b)[NL]) {
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
+            for (int fm = 0; fm < NL; ++fm)
 #pragma unroll
-            for (int fv = 0; fv < 4; ++fv)
-                acc[fv][fm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[fv]),
-                                                                      __builtin_bit_cast(bf16x8_t, b[fm]),
-                                                                      acc[fv][fm], 0, 0, 0);
-    };
-    static_assert(Cfg::KS == 2, "two K-steps per stage");
+                for (int fv = 0; fv < 4; ++fv)
+                    acc[fv][fm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[fv]),
+                                                                          __builtin_bit_cast(bf16x8_t, b[fm]),
+                                                                          acc[fv][fm], 0, 0, 0);
+        };
+        static_assert(Cfg::KS == 2, "two K-steps per stage");
 
 #pragma unroll
-    for (int i = -NSW; i < 0; ++i) issue_mid(i);
-    if (nk >= NSW) wait_vm<Cfg::PRO_WAIT>();
-    else wait_vm<0>();
-    stage_barrier();  // stage 0 landed in every wave
-    u32x4_t a0[4], b0[FM], a1[4], b1[FM];
-    read_frags(0, 0, a0, b0);
+        for (int i = -NSW; i < 0; ++i) issue_mid(i);
+        if (nk >= NSW) wait_vm<Cfg::PRO_WAIT>();
+        else wait_vm<0>();
+        stage_barrier();  // stage 0 landed in every wave
+        u32x4_t a0[4], b0[NL], a1[4], b1[NL];
+        read_frags(0, 0, a0, b0);
 
-    for (int kb = 0; kb < nk; ++kb) {
-        read_frags(kb, 1, a1, b1);
-        mma(a0, b0);
-        if (kb + 1 < nk) {
-            // this wave's loads of stage kb + 1 are done when only later ones remain;
-            // the last of those counted, W(kb + NSW - 1), exists iff kb + NSW - 1 < nk
-            if (kb + NSW - 1 < nk) wait_vm<Cfg::WAIT>();
-            else wait_vm<0>();
-            stage_barrier();  // stage kb + 1 landed everywhere; stage kb is in registers
-            issue_mid(kb);
-            read_frags(kb + 1, 0, a0, b0);
+        for (int kb = 0; kb < nk; ++kb) {
+            read_frags(kb, 1, a1, b1);
+            mma(a0, b0);
+            if (kb + 1 < nk) {
+                // this wave's loads of stage kb + 1 are done when only later ones remain;
+                // the last of those counted, W(kb + NSW - 1), exists iff kb + NSW - 1 < nk
+                if (kb + NSW - 1 < nk) wait_vm<Cfg::WAIT>();
+                else wait_vm<0>();
+                stage_barrier();  // stage kb + 1 landed everywhere; stage kb is in registers
+                issue_mid(kb);
+                read_frags(kb + 1, 0, a0, b0);
+            }
+            mma(a1, b1);
         }
-        mma(a1, b1);
-    }
+    };
+    // live fragments of this wave (uniform over the wave): all of them unless the
+    // tile's last positions are padding; the partial counts of the measured shapes
+    // (224 and 704 rows at 256 per tile: 6 and 4 of 8) have loops of their own
+    const int nlive = min(FM, max(1, (p.Meff - m0 - mw * (BM / 2) + 15) / 16));
+    if (FM == 8 && nlive == 6)
+        stage_loop(std::integral_constant<int, (FM == 8 ? 6 : FM)>{});
+    else if (FM == 8 && nlive == 4)
+        stage_loop(std::integral_constant<int, (FM == 8 ? 4 : FM)>{});
+    else
+        stage_loop(std::integral_constant<int, FM>{});
     __syncthreads();  // all stages read: the LDS is reused for the statistics
 
     // ------------------------------------------------------------- epilogue
