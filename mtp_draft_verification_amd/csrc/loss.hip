@@ -33,6 +33,8 @@
 namespace mtpv {
 namespace {
 
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kCap = 1120;                 // entries per wave buffer
@@ -281,15 +283,17 @@ struct F4 {
 template <bool VEC>
 __device__ __forceinline__ F4 load4(const float* row, int v, int V) {
     F4 r;
+    // non-temporal: each row is streamed once here (the gradient pass, if any, comes
+    // long after the row has left the caches)
     if (VEC) {
-        const float4 q = *reinterpret_cast<const float4*>(row + min(v, V - 4));
-        r.x[0] = q.x;
-        r.x[1] = q.y;
-        r.x[2] = q.z;
-        r.x[3] = q.w;
+        const f32x4_t q = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(row + min(v, V - 4)));
+        r.x[0] = q[0];
+        r.x[1] = q[1];
+        r.x[2] = q[2];
+        r.x[3] = q[3];
     } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) r.x[j] = row[min(v + j, V - 1)];
+        for (int j = 0; j < 4; ++j) r.x[j] = __builtin_nontemporal_load(row + min(v + j, V - 1));
     }
     return r;
 }
@@ -695,12 +699,14 @@ __global__ __launch_bounds__(kThreads) void loss_grad_kernel(LossArgs p) {
             const int r = (int)((sl >> (16 * j)) & 0xFFFFu);
             g[j] = r ? (float)((double)p.scale * ((double)q - pt[r])) : p.scale * q;
         }
+        // non-temporal stores: the gradient is written once and not read here again
         if (VEC) {
-            if (v < p.V) *reinterpret_cast<float4*>(grow + v) = make_float4(g[0], g[1], g[2], g[3]);
+            if (v < p.V)
+                __builtin_nontemporal_store(f32x4_t{g[0], g[1], g[2], g[3]}, reinterpret_cast<f32x4_t*>(grow + v));
         } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                if (v + j < p.V) grow[v + j] = g[j];
+                if (v + j < p.V) __builtin_nontemporal_store(g[j], grow + v + j);
         }
     }
 }

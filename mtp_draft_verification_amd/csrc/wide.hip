@@ -124,7 +124,11 @@ __device__ __forceinline__ void stage_barrier() {
 template <int CPR>
 __device__ __forceinline__ int chunk_swz(int r) { return (r / (16 / CPR)) % CPR; }
 
-template <int BM>
+// NTW: W is read by one workgroup only (one position chunk per vocabulary tile, K
+// not split), so its loads carry the non-temporal hint; with several chunks per tile
+// they share W through L2 and load it normally (a K-split launch measured slower
+// with the hint).
+template <int BM, bool NTW>
 __global__ __launch_bounds__(512, 1) void wide_kernel(LmHeadArgs p) {
     using Cfg = WideCfg<BM>;
     constexpr int NSW = Cfg::NSW;
@@ -220,7 +224,7 @@ __global__ __launch_bounds__(512, 1) void wide_kernel(LmHeadArgs p) {
         for (int i = 0; i < LPW_W; ++i) {
             const int k = kk * BK + 8 * w_chunk[i];
             const uint8_t* src = k < H ? w_row[i] + (size_t)k * 2 : w_row[i];
-            __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + i * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + i * 1024), 16, 0, NTW ? 2 : 0);  // 2: nt
         }
     };
     auto issue_x = [&](int kb) {
@@ -450,7 +454,7 @@ __global__ __launch_bounds__(512, 1) void wide_kernel(LmHeadArgs p) {
 
 template <int BM>
 hipError_t launch_bm(const Plan& plan, const LmHeadArgs& args, hipStream_t stream) {
-    auto kern = wide_kernel<BM>;
+    auto kern = (plan.MC == 1 && plan.ks == 1) ? wide_kernel<BM, true> : wide_kernel<BM, false>;
     const size_t lds = plan.lds;
     const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
