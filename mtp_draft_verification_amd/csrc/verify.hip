@@ -282,15 +282,20 @@ struct F4 {
     float a[4];
 };
 
+// VEC (V % 4 == 0, so every row starts 16-byte aligned): one 16-byte load; else four
+// 4-byte loads. A template parameter, not a run-time test: with both paths in one
+// function the compiler merged them into 4-byte loads.
+template <bool VEC>
 __device__ __forceinline__ F4 row_logit4(const float* logits, int row, int V, int v) {
     const float* base = logits + (size_t)max(row, 0) * V;
     F4 r;
-    if ((V & 3) == 0) {
-        const float4 x = *reinterpret_cast<const float4*>(base + min(v, V - 4));
-        r.a[0] = x.x;
-        r.a[1] = x.y;
-        r.a[2] = x.z;
-        r.a[3] = x.w;
+    if (VEC) {
+        typedef float f32x4_t __attribute__((ext_vector_type(4)));
+        const f32x4_t x = *reinterpret_cast<const f32x4_t*>(base + min(v, V - 4));
+        r.a[0] = x[0];
+        r.a[1] = x[1];
+        r.a[2] = x[2];
+        r.a[3] = x[3];
     } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) r.a[e] = base[min(v + e, V - 1)];
@@ -369,11 +374,13 @@ __device__ __forceinline__ void normalisers(const ResidualArgs& p, int j, double
     *rq = 1.0 / b;
 }
 
-// 16-byte loads per lane and row per loop trip in the sampling passes: all of them are
-// issued before the fp64 arithmetic.
+// 16-byte loads per lane and row per loop trip in the sampling passes. The loads of
+// the next trip are issued before the fp64 arithmetic of the current one (past the
+// chunk's end they re-read clamped addresses and are not used).
 constexpr int UR = 4;
 
 // Pass 1: per-chunk sums of exp(l/T - ref) for the job's p row and q row.
+template <bool VEC>
 __global__ __launch_bounds__(256) void zsum_kernel(ResidualArgs p) {
     __shared__ double sh[2][4];
     const int j = blockIdx.y, c = blockIdx.x;
@@ -385,14 +392,24 @@ __global__ __launch_bounds__(256) void zsum_kernel(ResidualArgs p) {
     const int e1 = min(p.V, t1 * 64);
     const bool has_q = job.row_q >= 0;
     double sp = 0.0, sq = 0.0;
+    F4 np[UR], nq[UR];
+    auto fetch = [&](int base) {
+#pragma unroll
+        for (int i = 0; i < UR; ++i) {
+            const int v = base + 1024 * i + 4 * tid;
+            np[i] = row_logit4<VEC>(p.logits, job.row_p, p.V, v);
+            nq[i] = row_logit4<VEC>(p.logits, has_q ? job.row_q : job.row_p, p.V, v);
+        }
+    };
+    fetch(t0 * 64);
     for (int base = t0 * 64; base < e1; base += 1024 * UR) {
         F4 lp[UR], lq[UR];
 #pragma unroll
         for (int i = 0; i < UR; ++i) {
-            const int v = base + 1024 * i + 4 * tid;
-            lp[i] = row_logit4(p.logits, job.row_p, p.V, v);
-            lq[i] = row_logit4(p.logits, has_q ? job.row_q : job.row_p, p.V, v);
+            lp[i] = np[i];
+            lq[i] = nq[i];
         }
+        fetch(base + 1024 * UR);
 #pragma unroll
         for (int i = 0; i < UR; ++i) {
             const int v = base + 1024 * i + 4 * tid;
@@ -421,6 +438,7 @@ __global__ __launch_bounds__(256) void zsum_kernel(ResidualArgs p) {
 // Pass 2: per-tile sums of the job's weights in the tile's fixed order. Each wave
 // load covers four consecutive tiles (1 KB of each row); wave w of the workgroup takes
 // tiles 4 w .. 4 w + 3 of every 16.
+template <bool VEC>
 __global__ __launch_bounds__(256) void tsum_kernel(ResidualArgs p) {
     const int j = blockIdx.y, c = blockIdx.x;
     const Job job = p.jobs[j];
@@ -431,14 +449,24 @@ __global__ __launch_bounds__(256) void tsum_kernel(ResidualArgs p) {
     const bool use_q = job.row_q >= 0;
     const int tpc = (p.ntiles + p.C - 1) / p.C;
     const int t0 = c * tpc, t1 = min(p.ntiles, t0 + tpc);
+    F4 np[UR], nq[UR];
+    auto fetch = [&](int tb) {
+#pragma unroll
+        for (int i = 0; i < UR; ++i) {
+            const int v = (tb + 16 * i) * 64 + 4 * q;
+            np[i] = row_logit4<VEC>(p.logits, job.row_p, p.V, v);
+            nq[i] = row_logit4<VEC>(p.logits, use_q ? job.row_q : job.row_p, p.V, v);
+        }
+    };
+    fetch(t0 + 4 * wave + g);
     for (int tb = t0 + 4 * wave + g; tb < t1; tb += 16 * UR) {  // uniform within each 16-lane group
         F4 lp[UR], lq[UR];
 #pragma unroll
         for (int i = 0; i < UR; ++i) {
-            const int v = (tb + 16 * i) * 64 + 4 * q;
-            lp[i] = row_logit4(p.logits, job.row_p, p.V, v);
-            lq[i] = row_logit4(p.logits, use_q ? job.row_q : job.row_p, p.V, v);
+            lp[i] = np[i];
+            lq[i] = nq[i];
         }
+        fetch(tb + 16 * UR);
 #pragma unroll
         for (int i = 0; i < UR; ++i) {
             const int t = tb + 16 * i;
@@ -450,6 +478,7 @@ __global__ __launch_bounds__(256) void tsum_kernel(ResidualArgs p) {
 }
 
 // Pass 3: locate u * (total weight) in the fixed-order sums and emit the token.
+template <bool VEC>
 __global__ __launch_bounds__(256) void search_kernel(ResidualArgs p) {
     __shared__ double wave_tot[4];
     __shared__ int sh_tile, sh_last, sh_pick;
@@ -472,7 +501,7 @@ __global__ __launch_bounds__(256) void search_kernel(ResidualArgs p) {
             const int g = lane >> 4, q = lane & 15;
             for (int tb = 4 * wave + g; tb < p.ntiles; tb += 16) {  // uniform within each 16-lane group
                 const int v = tb * 64 + 4 * q;
-                const F4 lp = row_logit4(p.logits, job.row_p, p.V, v);
+                const F4 lp = row_logit4<VEC>(p.logits, job.row_p, p.V, v);
                 const Lane4 w = lane_weights(lp, lp, v, p.V, false, p.inv_t, job, rp, rq);
                 const double incl = scan16(w.s, q);
                 if (q == 15 && tb < p.ntiles) ts[tb] = incl;
@@ -554,8 +583,8 @@ __global__ __launch_bounds__(256) void search_kernel(ResidualArgs p) {
             // (lanes 16..63 repeat the computation and are left out of the ballots)
             const int q = lane & 15;
             const int v = sh_pick * 64 + 4 * q;
-            const F4 lp = row_logit4(p.logits, job.row_p, p.V, v);
-            const F4 lq = row_logit4(p.logits, use_q ? job.row_q : job.row_p, p.V, v);
+            const F4 lp = row_logit4<VEC>(p.logits, job.row_p, p.V, v);
+            const F4 lq = row_logit4<VEC>(p.logits, use_q ? job.row_q : job.row_p, p.V, v);
             const Lane4 w = lane_weights(lp, lq, v, p.V, use_q, p.inv_t, job, rp, rq);
             const double incl = scan16(w.s, q);
             double excl = __shfl_up(incl, 1, 16);
@@ -609,15 +638,22 @@ hipError_t launch_decide(const Plan& plan, const DecideArgs& args, hipStream_t s
     return hipGetLastError();
 }
 
-hipError_t launch_residual(const Plan& plan, const ResidualArgs& args, hipStream_t stream) {
-    hipLaunchKernelGGL(zsum_kernel, dim3(args.C, args.NJ), dim3(256), 0, stream, args);
+template <bool VEC>
+hipError_t launch_residual_vec(const ResidualArgs& args, hipStream_t stream) {
+    hipLaunchKernelGGL(zsum_kernel<VEC>, dim3(args.C, args.NJ), dim3(256), 0, stream, args);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(tsum_kernel, dim3(args.C, args.NJ), dim3(256), 0, stream, args);
+    hipLaunchKernelGGL(tsum_kernel<VEC>, dim3(args.C, args.NJ), dim3(256), 0, stream, args);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(search_kernel, dim3(args.NJ), dim3(256), 0, stream, args);
+    hipLaunchKernelGGL(search_kernel<VEC>, dim3(args.NJ), dim3(256), 0, stream, args);
     return hipGetLastError();
+}
+
+hipError_t launch_residual(const Plan& plan, const ResidualArgs& args, hipStream_t stream) {
+    // the logit rows start 16-byte aligned when V % 4 == 0 (the buffer itself is)
+    const bool vec = (args.V & 3) == 0 && ((uintptr_t)args.logits & 15) == 0;
+    return vec ? launch_residual_vec<true>(args, stream) : launch_residual_vec<false>(args, stream);
 }
 
 hipError_t launch_probs(const ProbsArgs& args, hipStream_t stream) {
