@@ -105,6 +105,20 @@ struct WideCfg {
     static_assert(NSW - NSX <= 1 && PRO_WAIT < 64, "wait counts");
 };
 
+// Calls f(std::integral_constant<int, n>) for the run-time n in [0, N]: one
+// instantiation of f per count.
+template <int N, typename F>
+__device__ __forceinline__ void with_live(int n, F&& f) {
+    if constexpr (N == 0) {
+        f(std::integral_constant<int, 0>{});
+    } else {
+        if (n == N)
+            f(std::integral_constant<int, N>{});
+        else
+            with_live<N - 1>(n, f);
+    }
+}
+
 // Workgroup barrier for the stage ring. __syncthreads() would also make every wave
 // wait for all of its direct-to-LDS loads (vmcnt(0): its release fence covers them),
 // which drains the ring at every stage; the ring's own vmcnt wait already covers
@@ -269,7 +283,7 @@ __global__ __launch_bounds__(512, 1) void wide_kernel(LmHeadArgs p) {
     // fragments are not read and their MFMAs not issued (the accumulators stay 0).
     auto stage_loop = [&](auto nl_tag) {
         constexpr int NL = decltype(nl_tag)::value;
-        auto read_frags = [&](int kb, int s, u32x4_t (&a)[4], u32x4_t (&b)[NL]) {
+        auto read_frags = [&](int kb, int s, u32x4_t (&a)[4], u32x4_t (&b)[NL > 0 ? NL : 1]) {
             const uint8_t* wbase = wring + (kb % NSW) * Cfg::WSTAGE + (vw * 64) * ROWB;
             const uint8_t* xbase = xring + (kb % NSX) * Cfg::XSTAGE + (mw * (BM / 2)) * ROWB;
             const int fo = s == 0 ? frag_off0 : frag_off1;
@@ -278,7 +292,7 @@ __global__ __launch_bounds__(512, 1) void wide_kernel(LmHeadArgs p) {
 #pragma unroll
             for (int fm = 0; fm < NL; ++fm) b[fm] = *(const u32x4_t*)(xbase + fm * 16 * ROWB + fo);
         };
-        auto mma = [&](const u32x4_t (&a)[4], const u32x4_t (&b)[NL]) {
+        auto mma = [&](const u32x4_t (&a)[4], const u32x4_t (&b)[NL > 0 ? NL : 1]) {
 #pragma unroll
             for (int fm = 0; fm < NL; ++fm)
 #pragma unroll
@@ -294,7 +308,7 @@ __global__ __launch_bounds__(512, 1) void wide_kernel(LmHeadArgs p) {
         if (nk >= NSW) wait_vm<Cfg::PRO_WAIT>();
         else wait_vm<0>();
         stage_barrier();  // stage 0 landed in every wave
-        u32x4_t a0[4], b0[NL], a1[4], b1[NL];
+        u32x4_t a0[4], b0[NL > 0 ? NL : 1], a1[4], b1[NL > 0 ? NL : 1];
         read_frags(0, 0, a0, b0);
 
         for (int kb = 0; kb < nk; ++kb) {
@@ -313,15 +327,10 @@ __global__ __launch_bounds__(512, 1) void wide_kernel(LmHeadArgs p) {
         }
     };
     // live fragments of this wave (uniform over the wave): all of them unless the
-    // tile's last positions are padding; the partial counts of the measured shapes
-    // (224 and 704 rows at 256 per tile: 6 and 4 of 8) have loops of their own
-    const int nlive = min(FM, max(1, (p.Meff - m0 - mw * (BM / 2) + 15) / 16));
-    if (FM == 8 && nlive == 6)
-        stage_loop(std::integral_constant<int, (FM == 8 ? 6 : FM)>{});
-    else if (FM == 8 && nlive == 4)
-        stage_loop(std::integral_constant<int, (FM == 8 ? 4 : FM)>{});
-    else
-        stage_loop(std::integral_constant<int, FM>{});
+    // tile's last positions are padding; a wave with none still issues its share of
+    // the stage loads and meets every barrier
+    const int nlive = min(FM, max(0, (p.Meff - m0 - mw * (BM / 2) + 15) / 16));
+    with_live<FM>(nlive, stage_loop);
     __syncthreads();  // all stages read: the LDS is reused for the statistics
 
     // ------------------------------------------------------------- epilogue
