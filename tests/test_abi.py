@@ -203,3 +203,20 @@ def test_loss_call_validates_on_the_host():
     assert call(wsb=64) == -3
     assert call(ws=vp(WS + 16)) == -3
     assert call(ws=None) == -3
+
+
+def test_timing_hooks_on_the_host():
+    """mtpv_timing_enable takes the interval of timed calls (0 = off, n >= 1 = one
+    call in n) and rejects a negative one; reading with nothing timed touches no GPU."""
+    L = mv.lib()
+    assert L.mtpv_timing_enable(-1) == -1
+    assert L.mtpv_timing_enable(4) == 0
+    ms = ctypes.c_double(-1.0)
+    n = ctypes.c_int64(-1)
+    assert L.mtpv_timing_read(ctypes.byref(ms), ctypes.byref(n), 1) == 0
+    assert ms.value == 0.0 and n.value == 0
+    assert L.mtpv_timing_read(None, ctypes.byref(n), 0) == -5
+    assert L.mtpv_timing_enable(0) == 0
+    mv.timing_enable(True, every=16)
+    assert mv.timing_read() == (0.0, 0)
+    mv.timing_enable(False)
