@@ -30,6 +30,7 @@
 #include "mtpv_internal.h"
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include <climits>
@@ -461,14 +462,35 @@ __global__ __launch_bounds__(512, 1) void wide_kernel(LmHeadArgs p) {
     }
 }
 
+// Raises the kernel's dynamic-LDS limit to its ring size, once per device: the call
+// costs host time on every launch otherwise (and the limit never changes).
+template <int BM, bool NTW>
+hipError_t allow_lds() {
+    static std::atomic<uint64_t> done{0};  // bit d: done on device d (devices past 63: every call)
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = dev >= 0 && dev < 64 ? (1ull << dev) : 0ull;
+    if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+    e = hipFuncSetAttribute((const void*)wide_kernel<BM, NTW>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)WideCfg<BM>::LDS);
+    if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
+
+template <int BM, bool NTW>
+hipError_t launch_bm_nt(const Plan& plan, const LmHeadArgs& args, hipStream_t stream) {
+    const hipError_t e = allow_lds<BM, NTW>();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((wide_kernel<BM, NTW>), dim3(plan.grid), dim3(NT), plan.lds, stream, args);
+    return hipGetLastError();
+}
+
 template <int BM>
 hipError_t launch_bm(const Plan& plan, const LmHeadArgs& args, hipStream_t stream) {
-    auto kern = (plan.MC == 1 && plan.ks == 1) ? wide_kernel<BM, true> : wide_kernel<BM, false>;
-    const size_t lds = plan.lds;
-    const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(plan.grid), dim3(NT), lds, stream, args);
-    return hipGetLastError();
+    if (plan.lds > (size_t)WideCfg<BM>::LDS) return hipErrorInvalidConfiguration;
+    return (plan.MC == 1 && plan.ks == 1) ? launch_bm_nt<BM, true>(plan, args, stream)
+                                          : launch_bm_nt<BM, false>(plan, args, stream);
 }
 
 }  // namespace
