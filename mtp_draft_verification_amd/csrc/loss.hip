@@ -9,7 +9,7 @@
 //   grad   = scale * (softmax(s) - pt scattered on K)   (the teacher gets none)
 //
 // Selection kernel: one workgroup (4 waves) per row streams the teacher row and the
-// student row once with 16-byte loads. Each wave keeps, in LDS, the entries of its
+// student row once with non-temporal 16-byte loads. Each wave keeps, in LDS, the entries of its
 // share that beat a running threshold; when its buffer nears full it cuts it to about
 // its k best (a radix search for the k-th key, stopped early once the cut is within
 // a few entries of k) and raises the threshold, and publishes a bound under which

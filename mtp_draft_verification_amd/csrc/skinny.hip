@@ -13,9 +13,9 @@
 // heads: v_mfma_f32_4x4x1_16b_f32). Block b of lane (i + 4b) carries row i's
 // elements [16 b, 16 b + 16) bytes of the current 256-byte step; the matching B
 // lane (j + 4b) carries position j's same elements; block b accumulates the
-// partial dot products over its residue class of K, and a lane butterfly over the
-// 16 blocks at the end of each 4-row tile gives the full logits. Accumulation is
-// fp32 over all of H, fixed order.
+// partial dot products over its residue class of K, and a sum over the 16 blocks at
+// the end of each 4-row tile (DPP row rotations, then permlane swaps) gives the full
+// logits. Accumulation is fp32 over all of H, fixed order.
 //
 // The epilogue runs once per 4-row tile, in the middle of the stream (the next
 // tile's loads are already in flight): running max of l*c2 (log2 units), sum of

@@ -21,12 +21,15 @@
 //    makes the MFMA fragment reads (ds_read_b128, 16 rows per 16 lanes) free of bank
 //    conflicts;
 //  * wave w owns vocabulary rows 64 (w % 4) .. + 63 and positions (w / 4) BM / 2 ..
-//    + BM / 2 - 1 of the tile: 4 x BM / 32 accumulators of 16x16x32 bf16 MFMAs;
+//    + BM / 2 - 1 of the tile: 4 x BM / 32 accumulators of 16x16x32 bf16 MFMAs (a
+//    wave whose positions end inside its half skips the padded fragments);
 //  * after the last stage each wave folds its logits into per-position statistics
 //    (max of l * c2, sum of exp2, argmax), gathers the draft logits and writes the
 //    fp32 logits out when asked; the four vocabulary waves are merged into one
 //    partial per (position, vocabulary block).
-// Accumulation is fp32 over all of H in a fixed order; no split-K, no atomics.
+// Accumulation is fp32 over all of H in a fixed order, no atomics; the K-split launch
+// of the input fusion writes each slice's raw products, which ksum_kernel adds in
+// slice order.
 #include "mtpv_internal.h"
 
 #include <algorithm>
