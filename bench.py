@@ -435,7 +435,7 @@ def main():
     kern_ms, nlaunch = mv.timing_read(reset=True)
     mv.timing_enable(False)
     assert nlaunch == (K + every - 1) // every, (nlaunch, K, every)
-    if mv.device_error(ws) != 0:
+    if mv.get_device_error(ws) != 0:
         raise RuntimeError("device error word set during the benchmark")
 
     # per-call time of the whole call (every kernel of it), from events on the stream the

@@ -31,14 +31,14 @@
  *  - stream is a hipStream_t passed as void* (NULL = the default stream). Calls
  *    are asynchronous and stream ordered; nothing synchronizes the host.
  *  - workspace is caller-owned device memory of at least
- *    mtpv_workspace_bytes(mode, B, k, H, V, dtype) bytes, 256-byte aligned. Its
+ *    mtpv_workspace_bytes(B, k, H, V, dtype, mode) bytes, 256-byte aligned. Its
  *    contents need no initialisation and are scratch between calls; two calls
  *    in flight at once must not share one workspace.
  *  - Errors in sizes, pointers, alignment, dtype or workspace are found on the
  *    host before anything is enqueued and returned as a negative mtpv_status.
  *    A draft id outside [0, V) is not a host error (drafts live on the device):
  *    that draft counts as rejected and the call's device error word gets
- *    MTPV_DEVERR_DRAFT_RANGE (read it with mtpv_device_error).
+ *    MTPV_DEVERR_DRAFT_RANGE (read it with mtpv_get_device_error).
  *  - No exception crosses this boundary.
  */
 #ifndef MTPV_H_
@@ -63,9 +63,9 @@ typedef enum mtpv_status {
     MTPV_EALIGN = -2,     /* H not a multiple of 8, or a pointer not 16-byte aligned   */
     MTPV_EWORKSPACE = -3, /* workspace NULL, misaligned or smaller than required       */
     MTPV_EDTYPE = -4,     /* dtype is neither MTPV_BF16 nor MTPV_F32                   */
-    MTPV_ENULL = -5,      /* a required pointer is NULL                                */
-    MTPV_ELAUNCH = -6,    /* a kernel launch failed                                    */
-    MTPV_EDEVICE = -7     /* HIP runtime error (no device, bad stream, copy failed)    */
+    MTPV_ELAUNCH = -5,    /* a kernel launch failed                                    */
+    MTPV_EDEVICE = -6,    /* HIP runtime error (no device, bad stream, copy failed)    */
+    MTPV_ENULL = -7       /* a required pointer is NULL                                */
 } mtpv_status;
 
 typedef enum mtpv_dtype { MTPV_BF16 = 0, MTPV_F32 = 1 } mtpv_dtype;
@@ -105,10 +105,11 @@ MTPV_API int mtpv_version(void);
 MTPV_API const char* mtpv_status_string(int status);
 
 /*
- * Workspace bytes a call of the given mode and shape needs (0 if the shape is
- * invalid). Host only; no GPU needed.
+ * Workspace bytes a call of the given shape and mode needs (0 if the shape is
+ * invalid). mode: MTPV_MODE_GREEDY (0) or MTPV_MODE_SAMPLE (1) for the verify
+ * calls, MTPV_MODE_DRAFT (2) for spec_draft_sample. Host only; no GPU needed.
  */
-MTPV_API size_t mtpv_workspace_bytes(int mode, int B, int k, int H, int V, int dtype);
+MTPV_API size_t mtpv_workspace_bytes(int B, int k, int H, int V, int dtype, int mode);
 
 /*
  * Host-only argument check shared by every call; returns what the call itself
@@ -124,8 +125,8 @@ MTPV_API int mtpv_check_args(int mode, int B, int k, int H, int V, int dtype, do
 
 /*
  * Greedy verification.
- * "The verifier accepts the longest prefix that agrees with the target model",
- * so greedy speculative decoding returns exactly the tokens of ordinary greedy
+ * The drafts are kept up to the first one the target's argmax disagrees with,
+ * which makes greedy speculative decoding emit the same sequence as plain greedy
  * decoding ("The Tiny Draft Model Hidden Inside Qwen", section "How the draft
  * becomes real output"). For each request b:
  *   g_j = argmax_v l(target row j)  (lowest id on ties), j = 0..k
@@ -211,7 +212,7 @@ MTPV_API int spec_verify_sample_ragged(const void* target_hidden, const void* dr
  * returns for (target_hidden, draft_tokens) and accepted_len_sample /
  * out_tokens_sample exactly what spec_verify_sample returns. draft_len as in
  * spec_verify_sample_ragged (NULL = k everywhere). The four output arrays must
- * not overlap. Workspace: mtpv_workspace_bytes(MTPV_MODE_SAMPLE, ...). Debug
+ * not overlap. Workspace: mtpv_workspace_bytes(..., MTPV_MODE_SAMPLE). Debug
  * exports are those of the stochastic pass.
  */
 MTPV_API int spec_verify_dual(const void* target_hidden, const void* draft_hidden, const void* W_lm,
@@ -281,7 +282,7 @@ MTPV_API int mtp_draft_loss_topk(const float* teacher, const float* student, int
  * the weights"); a chained drafter calls this once per depth with kd = 1 and
  * depth0 = depth, and the verify call then sees the same Philox stream.
  * draft_hidden [B, kd, H]; draft_tokens [B, kd] int32 (output).
- * Workspace: mtpv_workspace_bytes(MTPV_MODE_DRAFT, B, kd, H, V, dtype).
+ * Workspace: mtpv_workspace_bytes(B, kd, H, V, dtype, MTPV_MODE_DRAFT).
  */
 MTPV_API int spec_draft_sample(const void* draft_hidden, const void* W_lm, int B, int kd, int depth0,
                       int H, int V, int dtype, double temperature, uint64_t seed, uint64_t offset,
@@ -289,10 +290,11 @@ MTPV_API int spec_draft_sample(const void* draft_hidden, const void* W_lm, int B
                       const mtpv_debug* debug, void* stream);
 
 /*
- * Reads the device error word of the last call that used this workspace:
- * waits for the stream, then copies the word to *err (0 = no error).
+ * Reads the device error word (the sticky MTPV_DEVERR_* bits) of the last call
+ * that used this workspace: waits for the stream, then copies the word to *err
+ * (0 = no error).
  */
-MTPV_API int mtpv_device_error(const void* workspace, int32_t* err, void* stream);
+MTPV_API int mtpv_get_device_error(const void* workspace, int32_t* err, void* stream);
 
 /*
  * Measurement hooks. mtpv_timing_enable(every) with every >= 1 makes one call in

@@ -32,7 +32,7 @@ DEVERR_TOKEN_RANGE = 4
 LOSS_MAX_TOPK = 512
 
 STATUS = {0: "MTPV_OK", -1: "MTPV_EINVAL", -2: "MTPV_EALIGN", -3: "MTPV_EWORKSPACE", -4: "MTPV_EDTYPE",
-          -5: "MTPV_ENULL", -6: "MTPV_ELAUNCH", -7: "MTPV_EDEVICE"}
+          -5: "MTPV_ELAUNCH", -6: "MTPV_EDEVICE", -7: "MTPV_ENULL"}
 
 
 class MtpvError(RuntimeError):
@@ -70,7 +70,7 @@ _SIGNATURES = {
     "mtp_input_fuse": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _d, _vp, _vp, _sz, _vp]),
     "mtpv_loss_workspace_bytes": (_sz, [_i, _i]),
     "mtp_draft_loss_topk": (_i, [_vp, _vp, _i, _i, _i, ctypes.c_float, _vp, _vp, _vp, _vp, _sz, _vp]),
-    "mtpv_device_error": (_i, [_vp, ctypes.POINTER(ctypes.c_int32), _vp]),
+    "mtpv_get_device_error": (_i, [_vp, ctypes.POINTER(ctypes.c_int32), _vp]),
     "mtpv_timing_enable": (_i, [_i]),
     "mtpv_timing_read": (_i, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), _i]),
     "mtpv_copy_bytes": (_i, [_vp, _vp, _sz, _vp]),
@@ -128,15 +128,15 @@ def _contig(name, t):
         raise ValueError(f"{name} must be contiguous")
 
 
-def workspace_bytes(mode, B, k, H, V, dtype):
-    """Workspace size in bytes (0 for an invalid shape). dtype: DTYPE_BF16 / DTYPE_F32."""
-    return int(lib().mtpv_workspace_bytes(mode, B, k, H, V, dtype))
+def workspace_bytes(B, k, H, V, dtype, mode):
+    """Workspace size in bytes (0 for an invalid shape). dtype: DTYPE_BF16 / DTYPE_F32; mode: MODE_*."""
+    return int(lib().mtpv_workspace_bytes(B, k, H, V, dtype, mode))
 
 
 def alloc_workspace(mode, B, k, H, V, dtype, device):
     """Allocate a workspace tensor for a call shape (done once, outside the hot loop)."""
     import torch
-    n = workspace_bytes(mode, B, k, H, V, dtype)
+    n = workspace_bytes(B, k, H, V, dtype, mode)
     if n == 0:
         _check(-1, "workspace_bytes")
     return torch.empty(n, dtype=torch.uint8, device=device)
@@ -294,10 +294,11 @@ def spec_draft_sample(draft_hidden, W, temperature, seed, offset, depth0, draft_
     _check(st, "spec_draft_sample")
 
 
-def device_error(workspace, stream=None):
+def get_device_error(workspace, stream=None):
     """Waits for the stream and returns the last call's device error word."""
     err = ctypes.c_int32(0)
-    _check(lib().mtpv_device_error(_ptr(workspace), ctypes.byref(err), _stream(stream)), "mtpv_device_error")
+    _check(lib().mtpv_get_device_error(_ptr(workspace), ctypes.byref(err), _stream(stream)),
+           "mtpv_get_device_error")
     return int(err.value)
 
 

@@ -255,7 +255,7 @@ const char* mtpv_status_string(int status) {
     }
 }
 
-size_t mtpv_workspace_bytes(int mode, int B, int k, int H, int V, int dtype) {
+size_t mtpv_workspace_bytes(int B, int k, int H, int V, int dtype, int mode) {
     Plan p;
     if (make_plan(mode, B, k, H, V, dtype, &p) != MTPV_OK) return 0;
     return p.total;
@@ -424,7 +424,7 @@ int spec_draft_sample(const void* draft_hidden, const void* W_lm, int B, int kd,
                nullptr, workspace, debug, static_cast<hipStream_t>(stream));
 }
 
-int mtpv_device_error(const void* workspace, int32_t* err, void* stream) {
+int mtpv_get_device_error(const void* workspace, int32_t* err, void* stream) {
     if (workspace == nullptr || err == nullptr) return MTPV_ENULL;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (hipStreamSynchronize(s) != hipSuccess) return MTPV_EDEVICE;

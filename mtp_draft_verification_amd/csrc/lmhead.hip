@@ -1,21 +1,21 @@
-// LM-head streaming kernel with the fused vocab-split softmax / argmax epilogue.
+// LM-head tile kernel for an fp32 head with more than 16 positions (the tiny
+// fp32-head workload), with the fused vocab-split softmax / argmax epilogue. bf16
+// heads take the streaming kernel (skinny.hip) or the LDS-tiled kernel (wide.hip).
 //
 // The verify step pushes every target verify position and every drafter
 // position through the one shared vocabulary head ("The Tiny Draft Model Hidden
 // Inside Qwen", sections "One step deeper than the main model" and "How the
-// draft becomes real output"). Decoding is weight-read bound and one read of the
-// weights serves all positions of the pass ("Speculative Decoding and MTP: Why
-// Guessing Is Free", section "The part that got me"), so the kernel is built
-// around reading W_lm [V, H] from HBM exactly once:
+// draft becomes real output"); one read of the weights serves all positions of
+// the pass ("Speculative Decoding and MTP: Why Guessing Is Free", section "The
+// part that got me"):
 //
-//  * a workgroup owns 64*VA consecutive vocabulary rows and one chunk of up to
-//    16*NT rows (positions); each of its 4 waves owns 16*VA vocabulary rows;
+//  * a workgroup owns 64 consecutive vocabulary rows and one chunk of up to
+//    16*NT rows (positions); each of its 4 waves owns 16 vocabulary rows;
 //  * the positions' hidden states are staged in LDS (all of H at once when they
 //    fit, else in K chunks), W goes from HBM straight into MFMA A-operand
 //    registers with 16-byte loads, PF steps ahead of its use;
-//  * bf16: one v_mfma_f32_16x16x32_bf16 per 16-byte fragment pair; fp32: four
-//    v_mfma_f32_16x16x4_f32. Accumulation is fp32 over the whole of H (no
-//    split-K), in a fixed order;
+//  * four v_mfma_f32_16x16x4_f32 per 16-byte fragment pair. Accumulation is fp32
+//    over the whole of H (no split-K), in a fixed order;
 //  * the epilogue reduces each position over the workgroup's vocabulary rows
 //    to {max of l/T (log2 units), sum of exp, argmax (lowest id on ties)},
 //    gathers the logit of the position's draft token, and optionally writes the
@@ -33,20 +33,11 @@
 namespace mtpv {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 template <int ES>
 struct Mma;
-
-template <>
-struct Mma<2> {  // bf16 storage: 8 elements per 16-byte fragment, K = 32 per step
-    __device__ __forceinline__ static f32x4_t run(u32x4_t a, u32x4_t b, f32x4_t c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                        __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-    }
-};
 
 template <>
 struct Mma<4> {  // fp32 storage: 4 elements per fragment, K = 16 per step
@@ -310,23 +301,7 @@ hipError_t launch_one(const Plan& plan, const LmHeadArgs& args, hipStream_t stre
 }  // namespace
 
 hipError_t launch_lmhead(const Plan& plan, const LmHeadArgs& args, hipStream_t stream) {
-    if (plan.es == 2) {
-        if (plan.va == 2) {
-            switch (plan.nt) {
-                case 1: return launch_one<2, 2, 1>(plan, args, stream);
-                case 2: return launch_one<2, 2, 2>(plan, args, stream);
-                case 4: return launch_one<2, 2, 4>(plan, args, stream);
-                case 8: return launch_one<2, 2, 8>(plan, args, stream);
-                default: break;
-            }
-        } else if (plan.va == 1) {
-            switch (plan.nt) {
-                case 1: return launch_one<2, 1, 1>(plan, args, stream);
-                case 2: return launch_one<2, 1, 2>(plan, args, stream);
-                default: break;
-            }
-        }
-    } else if (plan.es == 4 && plan.va == 1) {
+    if (plan.es == 4 && plan.va == 1) {
         switch (plan.nt) {
             case 1: return launch_one<4, 1, 1>(plan, args, stream);
             case 2: return launch_one<4, 1, 2>(plan, args, stream);

@@ -111,15 +111,11 @@ int make_plan(int mode, int B, int k, int H, int V, int dtype, Plan* pl) {
         p.vblock = 0;
     }
     if (p.kind == KIND_TILE) {
-        // LM-head tile: positions in chunks of 16*nt, 16*va vocab rows per wave.
+        // LM-head tile (fp32 heads only; every bf16 shape took one of the kernels
+        // above): positions in chunks of 16*nt, 16 vocab rows per wave.
         const int need = (p.Meff + 15) / 16;
-        if (p.es == 2) {
-            p.nt = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
-            p.va = p.nt == 1 ? 1 : 2;
-        } else {
-            p.va = 1;
-            p.nt = need <= 1 ? 1 : 2;
-        }
+        p.va = 1;
+        p.nt = need <= 1 ? 1 : 2;
         p.vblock = 64 * p.va;
         p.S = (V + p.vblock - 1) / p.vblock;
         p.MC = (p.Meff + 16 * p.nt - 1) / (16 * p.nt);

@@ -4,7 +4,7 @@
 // decide_kernel (one workgroup per request) merges the LM-head kernel's
 // per-(row, vocab block) partials in a fixed order into per-row {max, sum of
 // exp, argmax}, takes the acceptance decisions slot by slot and scans for the
-// first rejection ("accept the longest correct prefix", "Speculative Decoding
+// first rejection (the correct prefix is kept: "Speculative Decoding
 // and MTP: Why Guessing Is Free", section "Speculative decoding: draft, then
 // verify"; "The Tiny Draft Model Hidden Inside Qwen", section "How the draft
 // becomes real output"), writes accepted_len / out_tokens and, when a token

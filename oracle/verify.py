@@ -51,8 +51,8 @@ def lm_head_logits(X, W):
 def softmax(L, T=1.0):
     """Row distribution softmax(L / T) over the last axis, fp64, max-subtracted.
 
-    The verifier "produces its own distribution at every position in the draft"
-    ("The Tiny Draft Model Hidden Inside Qwen", section "How the draft becomes real
+    The verifier computes a distribution of its own at each drafted position ("The
+    Tiny Draft Model Hidden Inside Qwen", section "How the draft becomes real
     output"). The temperature T is applied to both target and drafter rows.
     """
     Z = np.asarray(L, dtype=np.float64) / float(T)
@@ -86,12 +86,11 @@ def _assemble(drafts, a, fill):
 def greedy_verify(Lt, drafts):
     """Greedy verification: keep the longest prefix that agrees with the target argmax.
 
-    "The verifier accepts the longest prefix that agrees with the target model ...
-    Greedy decoding therefore returns the same tokens as ordinary greedy decoding"
-    ("The Tiny Draft Model Hidden Inside Qwen", section "How the draft becomes real
-    output"); accept the longest correct prefix and throw away the rest
-    ("Speculative Decoding and MTP: Why Guessing Is Free", section "Speculative
-    decoding: draft, then verify").
+    The drafts are kept up to the first one the target disagrees with, so greedy
+    speculative decoding emits the plain greedy sequence ("The Tiny Draft Model
+    Hidden Inside Qwen", section "How the draft becomes real output"); the drafts
+    after the first wrong one are discarded ("Speculative Decoding and MTP: Why
+    Guessing Is Free", section "Speculative decoding: draft, then verify").
 
     Lt [B, k+1, V] target logits; drafts [B, k]. argmax ties go to the lowest id.
     Returns (a [B], out [B, k+1], diag) where diag["argmax"] is [B, k+1] and
@@ -162,8 +161,10 @@ def stochastic_verify(P, Q, drafts, u_acc, u_res):
     The pages require the surviving tokens to be distributed exactly as the target
     alone would produce them ("It's exact, not approximate"; "The Tiny Draft Model
     Hidden Inside Qwen", section "How the draft becomes real output": first
-    rejection -> corrected replacement distribution; "Guess three tokens correctly
-    and you've produced four"). Works on float64 or exact-rational object arrays.
+    rejection -> corrected replacement distribution; k correct drafts yield k + 1
+    tokens, "Speculative Decoding and MTP: Why Guessing Is Free", section
+    "Speculative decoding: draft, then verify"). Works on float64 or exact-rational
+    object arrays.
 
     Returns (a [B], out [B, k+1], diag).
     """

@@ -90,7 +90,7 @@ def gpu_run(case, mode, drafts_d=None, xd_d=None, debug=True):
     else:
         mv.spec_verify_sample(case.xt_d, xd_d, case.W_d, drafts_d, wl.T, wl.seed, case.step, alen, out, ws,
                               debug=dbg)
-    err = mv.device_error(ws)
+    err = mv.get_device_error(ws)
     torch.cuda.synchronize()
     res = {"a": alen.cpu().numpy(), "out": out.cpu().numpy(), "err": err}
     for n, t in ex.items():

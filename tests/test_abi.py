@@ -40,7 +40,7 @@ def test_status_strings():
 
 
 def ws_bytes(mode=0, B=2, k=3, H=256, V=1000, dtype=0):
-    return mv.workspace_bytes(mode, B, k, H, V, dtype)
+    return mv.workspace_bytes(B, k, H, V, dtype, mode)
 
 
 def test_workspace_sizes():
@@ -53,7 +53,7 @@ def test_workspace_sizes():
     assert ws_bytes(0, V=0) == 0 and ws_bytes(0, H=12) == 0 and ws_bytes(5) == 0
     assert ws_bytes(2, k=0) == 0
     # full-size shapes fit comfortably in one GPU's HBM
-    assert mv.workspace_bytes(1, 256, 3, 7168, 129280, 0) < 2 << 30
+    assert mv.workspace_bytes(256, 3, 7168, 129280, 0, 1) < 2 << 30
 
 
 def check(**kw):
@@ -84,9 +84,9 @@ def test_valid_arguments_pass():
     (dict(H=260), -2), (dict(W=A + 8), -2), (dict(target_hidden=A + 4), -2), (dict(drafts=A + 2), -2),
     (dict(workspace=None), -3), (dict(workspace=WS + 64), -3), (dict(ws_bytes=16), -3),
     (dict(dtype=2), -4), (dict(dtype=-1), -4),
-    (dict(W=None), -5), (dict(target_hidden=None), -5), (dict(drafts=None), -5),
-    (dict(accepted_len=None), -5), (dict(out_tokens=None), -5),
-    (dict(mode=1, draft_hidden=None), -5), (dict(mode=2, draft_hidden=None), -5),
+    (dict(W=None), -7), (dict(target_hidden=None), -7), (dict(drafts=None), -7),
+    (dict(accepted_len=None), -7), (dict(out_tokens=None), -7),
+    (dict(mode=1, draft_hidden=None), -7), (dict(mode=2, draft_hidden=None), -7),
 ])
 def test_each_error_code(kw, code):
     assert check(**kw) == code
@@ -136,11 +136,11 @@ def test_ragged_and_dual_calls_validate_on_the_host():
                                        vp(A), vp(A), vp(WS), 1 << 30, None, None) == -2
     # dual: missing greedy outputs, misaligned greedy output, missing drafter rows
     assert L.spec_verify_dual(vp(A), vp(A), vp(A), vp(A), None, 2, 3, 256, 1000, 0, 1.0, 0, 0, None, vp(A),
-                              vp(A), vp(A), vp(WS), 1 << 30, None, None) == -5
+                              vp(A), vp(A), vp(WS), 1 << 30, None, None) == -7
     assert L.spec_verify_dual(vp(A), vp(A), vp(A), vp(A), None, 2, 3, 256, 1000, 0, 1.0, 0, 0, vp(A + 2), vp(A),
                               vp(A), vp(A), vp(WS), 1 << 30, None, None) == -2
     assert L.spec_verify_dual(vp(A), None, vp(A), vp(A), None, 2, 3, 256, 1000, 0, 1.0, 0, 0, vp(A), vp(A),
-                              vp(A), vp(A), vp(WS), 1 << 30, None, None) == -5
+                              vp(A), vp(A), vp(WS), 1 << 30, None, None) == -7
     assert L.spec_verify_dual(vp(A), vp(A), vp(A), vp(A), None, 2, 3, 256, 1000, 0, 1.0, 0, 0, vp(A), vp(A),
                               vp(A), vp(A), vp(WS), ws_small, None, None) == -3
 
@@ -164,8 +164,8 @@ def test_fuse_call_validates_on_the_host():
     assert call(eps=-1.0) == -1
     assert call(eps=float("nan")) == -1
     assert call(H=260) == -2
-    assert call(embed=None) == -5
-    assert call(W=None) == -5
+    assert call(embed=None) == -7
+    assert call(W=None) == -7
     assert call(out=vp(A + 4)) == -2
     assert call(tokens=vp(A + 2)) == -2
     assert call(hidden=vp(A + 8)) == -2
@@ -195,8 +195,8 @@ def test_loss_call_validates_on_the_host():
     assert call(k=mv.LOSS_MAX_TOPK + 1, V=4096) == -1
     assert call(scale=float("inf")) == -1
     assert call(N=0, t=None, s=None, loss=None) == 0   # nothing to do
-    assert call(t=None) == -5
-    assert call(loss=None) == -5
+    assert call(t=None) == -7
+    assert call(loss=None) == -7
     assert call(s=vp(A + 2)) == -2
     assert call(grad=vp(A + 1)) == -2
     assert call(idx=vp(A + 2)) == -2
@@ -215,8 +215,33 @@ def test_timing_hooks_on_the_host():
     n = ctypes.c_int64(-1)
     assert L.mtpv_timing_read(ctypes.byref(ms), ctypes.byref(n), 1) == 0
     assert ms.value == 0.0 and n.value == 0
-    assert L.mtpv_timing_read(None, ctypes.byref(n), 0) == -5
+    assert L.mtpv_timing_read(None, ctypes.byref(n), 0) == -7
     assert L.mtpv_timing_enable(0) == 0
     mv.timing_enable(True, every=16)
     assert mv.timing_read() == (0.0, 0)
     mv.timing_enable(False)
+
+
+def test_status_values_match_the_header():
+    """The status codes of the boundary, as the header declares them: the six codes
+    of the verify calls keep fixed values, ENULL comes after them."""
+    text = open(HEADER).read()
+    decl = dict((n, int(v)) for n, v in re.findall(r"(MTPV_E?\w+)\s*=\s*(-?\d+)\s*[,}/]", text))
+    want = {"MTPV_OK": 0, "MTPV_EINVAL": -1, "MTPV_EALIGN": -2, "MTPV_EWORKSPACE": -3, "MTPV_EDTYPE": -4,
+            "MTPV_ELAUNCH": -5, "MTPV_EDEVICE": -6, "MTPV_ENULL": -7}
+    for name, value in want.items():
+        assert decl.get(name) == value, (name, decl.get(name))
+        assert mv.STATUS[value] == name
+    assert mv.lib().mtpv_get_device_error(None, None, None) == -7
+
+
+def test_workspace_bytes_argument_order():
+    """mtpv_workspace_bytes(B, k, H, V, dtype, mode): the sample-mode workspace holds the
+    fp32 spill of B(k+1) + Bk rows; greedy holds none."""
+    L = mv.lib()
+    B, k, H, V = 3, 2, 64, 4000
+    s = L.mtpv_workspace_bytes(B, k, H, V, 0, 1)
+    g = L.mtpv_workspace_bytes(B, k, H, V, 0, 0)
+    assert s - g >= (B * (k + 1) + B * k) * V * 4
+    assert L.mtpv_workspace_bytes(B, k, H, V, 0, 3) == 0   # no such mode
+    assert L.mtpv_workspace_bytes(B, k, H, V, 2, 0) == 0   # no such dtype

@@ -77,7 +77,7 @@ def _gpu_call(wl, mode, Wd, xt_d, xd_d, drafts_d, step, debug=None):
         mv.spec_verify_greedy(xt_d, Wd, drafts_d, alen, out, ws, debug=debug)
     else:
         mv.spec_verify_sample(xt_d, xd_d, Wd, drafts_d, wl.T, wl.seed, step, alen, out, ws, debug=debug)
-    err = mv.device_error(ws)
+    err = mv.get_device_error(ws)
     torch.cuda.synchronize()
     return alen.cpu().numpy(), out.cpu().numpy(), err
 

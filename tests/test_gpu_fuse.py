@@ -36,7 +36,7 @@ def _run(H, V, B, step, bad=()):
     ws = mv.alloc_fuse_workspace(B, H, dev())
     mv.mtp_input_fuse(torch.from_numpy(tokens).to(dev()), _bf16_dev(E), _bf16_dev(h), _bf16_dev(ge), _bf16_dev(gh),
                       _bf16_dev(W), 1e-6, out, ws)
-    err = mv.device_error(ws)
+    err = mv.get_device_error(ws)
     torch.cuda.synchronize()
     dec = oracle.decode_bf16
     y, x = oracle.mtp_input_fuse(tokens, dec(E), dec(h), dec(ge), dec(gh), dec(W), 1e-6)

@@ -102,7 +102,7 @@ def _call_ragged(case, mode, drafts_d, klen_d):
     else:
         mv.spec_verify_sample_ragged(case.xt_d, case.xd_d, case.W_d, drafts_d, klen_d, case.wl.T, case.wl.seed,
                                      case.step, alen, out, ws)
-    err = mv.device_error(ws)
+    err = mv.get_device_error(ws)
     torch.cuda.synchronize()
     return alen.cpu().numpy(), out.cpu().numpy(), err
 
@@ -180,7 +180,7 @@ def test_dual_call(shape, ragged, cache):
         os_ = torch.full((B, k + 1), -7, dtype=torch.int32, device=dev())
         ws = mv.alloc_workspace(mv.MODE_SAMPLE, B, k, wl.H, wl.V, mv.DTYPE_BF16, dev())
         mv.spec_verify_dual(case.xt_d, case.xd_d, Wd, drafts_d, klen_d, wl.T, wl.seed, step, ag, og, as_, os_, ws)
-        assert mv.device_error(ws) == 0
+        assert mv.get_device_error(ws) == 0
         # the stochastic outcome is the sample call's, bit for bit
         a2, o2, _ = _call_ragged(case, "sample", drafts_d, klen_d)
         assert np.array_equal(as_.cpu().numpy(), a2) and np.array_equal(os_.cpu().numpy(), o2)

@@ -10,7 +10,8 @@ what the oracle emits and compares it with what the pages fix:
   approximate", "Speculative Decoding and MTP: Why Guessing Is Free");
 * a chain of k slots: P(a >= j) = prod_{i<j} sum_v min(p_i, q_i) and, given a >= j,
   the token at slot j is distributed as p_j; with k correct guesses a bonus token
-  comes from p_k ("Guess three tokens correctly and you've produced four");
+  comes from p_k (k correct drafts yield k + 1 tokens: "Speculative Decoding and MTP:
+  Why Guessing Is Free", section "Speculative decoding: draft, then verify");
 * a context-dependent target: the first two emitted tokens follow the target's
   autoregressive product law.
 
