@@ -1,6 +1,7 @@
 """Benchmark of the vocab-side verify step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--mode greedy|sample]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5] [--mode greedy|sample]
+    python bench.py --all [--jsonl FILE]       (one JSON line per workload and mode)
     python bench.py --op fuse --workload 3     (MTP input fusion at that width and batch)
     python bench.py --op loss                  (top-k soft cross-entropy draft loss + gradient)
     python bench.py --sweep                    (greedy verify time against M_eff, one line per M)
@@ -8,18 +9,20 @@
 One step = one verify call (the whole hot path: LM-head stream + fused softmax/argmax
 epilogue, cross-block combine, acceptance decisions and prefix scan, and in sample
 mode the fp64 correction/bonus draws) over one batch of synthetic inputs already
-resident in HBM. The default workload is single-stream decode: H=4096, V=151936,
-bf16 head, B=1 request, k=3 drafts, greedy verification. Inputs cycle through a pool
+resident in HBM. The default workload is the largest one that fits one GPU, the
+large-batch rollout: H=7168, V=129280, bf16 head, B=256 requests, k=3 drafts,
+stochastic verification at T=1 (1792 head rows per call). Inputs cycle through a pool
 of distinct seeded steps; drafts are drawn beforehand by the library's own drafter
 call (Philox word 2) from the drafter hidden states.
 
 Prints one JSON line: verified positions/s (value), accepted and emitted tokens/s, the
 per-depth acceptance P(a >= d) and the accepted-length histogram, the whole call's time
 (median, p10, p90 from events on the call's stream, in a second pass over the same
-inputs after the timed loop), the LM-head kernel's
-achieved HBM bandwidth against the 8 TB/s peak (kernel time from HIP events recorded by
-the library on the call's stream around one launch in 16 of the timed loop), the
-hardware-counter traffic recorded under
+inputs after the timed loop), the LM-head kernel against its roofline (HBM bandwidth
+against 8 TB/s when the algorithmic bytes take longer at that rate than the
+algorithmic flops at 2.5 PFLOP/s, else bf16 MFMA throughput against 2.5 PFLOP/s;
+kernel time from HIP events recorded by the library on the call's stream around a
+sample of the timed loop's launches), the hardware-counter traffic recorded under
 profiles/ when it was taken on the current kernel source, and the CPU oracle timed on a
 bounded sample of the same workload, which also checks the GPU's outcomes of the steps it
 shares with the timed loop (parity_vs_oracle).
@@ -120,6 +123,28 @@ def algorithmic(wl, mode):
     return bytes_, flops
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _blas_vendor():
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                return f"{i.get('internal_api')} {i.get('version')} ({i.get('architecture')})"
+    except Exception:
+        pass
+    return "unknown"
+
+
 def _blas_cores():
     try:
         from threadpoolctl import threadpool_info
@@ -169,11 +194,32 @@ def cpu_baseline(wl, mode, W_store, budget_s, gpu=None):
     pos = wl.B * (wl.k + 1) * n
     out = {"value": pos / t_total, "unit": "positions/s", "cores": cores, "kind": "oracle",
            "sample": f"{n} steps of the same workload ({pos} verified positions), fp64 numpy, "
-                     f"{t_total:.1f} s of oracle time; accepted tokens/s {accepted / t_total:.3g}"}
+                     f"{t_total:.1f} s of oracle time; accepted tokens/s {accepted / t_total:.3g}",
+           "cpu_model": _cpu_model(), "blas": _blas_vendor()}
     parity = None
     if gpu is not None:
         parity = {"steps": cmp_steps, "positions": cmp_pos, "excused": cmp_exc, "mismatched_requests": cmp_fail}
     return out, parity
+
+
+def roofline_of(alg_bytes, alg_flops, kern_s, traffic_bytes=None):
+    """The roofline the LM-head kernel sits on, and where it is against it. The bound is
+    HBM when moving the algorithmic bytes at 8 TB/s takes longer than the algorithmic
+    flops at 2.5 PFLOP/s, else bf16 MFMA. Both fractions are given either way."""
+    hbm = alg_bytes / kern_s / 1e9
+    tflops = alg_flops / kern_s / 1e12
+    mfma_bound = alg_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > alg_bytes / (HBM_PEAK_GBS * 1e9)
+    r = ({"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+          "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)} if mfma_bound else
+         {"bound": "hbm", "achieved": round(hbm, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+          "frac": round(hbm / HBM_PEAK_GBS, 4)})
+    r["traffic"] = None if traffic_bytes is None else round(traffic_bytes / kern_s / 1e9, 1)
+    r["traffic_unit"] = "GB/s"
+    r.update({"kernel_us": round(kern_s * 1e6, 2), "algorithmic_bytes_per_launch": alg_bytes,
+              "algorithmic_flops_per_launch": alg_flops, "hbm_gbs": round(hbm, 1),
+              "hbm_frac": round(hbm / HBM_PEAK_GBS, 4), "mfma_tflops": round(tflops, 2),
+              "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)})
+    return r
 
 
 def timing_every(steps):
@@ -331,7 +377,8 @@ def bench_loss(args):
                 grad_bad += int((np.abs(grad[rows].cpu().numpy() - G[0]) > tol).any())
             rows += 1
         line["cpu_baseline"] = {"value": round(rows / el, 2), "unit": "rows/s", "cores": _blas_cores(),
-                                "kind": "oracle", "sample": f"{rows} rows of the same call (loss + gradient)"}
+                                "kind": "oracle", "sample": f"{rows} rows of the same call (loss + gradient)",
+                                "cpu_model": _cpu_model(), "blas": _blas_vendor()}
         line["parity_vs_oracle"] = {"rows": rows, "kept_id_mismatches": idx_bad, "loss_out_of_bound": loss_bad,
                                     "gradient_rows_checked": min(rows, 8), "gradient_rows_out_of_bound": grad_bad}
     print(json.dumps(line), flush=True)
@@ -340,9 +387,9 @@ def bench_loss(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2,
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--workload", type=int, default=5,
                     help="1 tiny fp32, 2 decode, 3 batched sampling, 4 depth-5 chain, 5 rollout")
     ap.add_argument("--mode", choices=["greedy", "sample"], default=None)
     ap.add_argument("--pool", type=int, default=32, help="distinct seeded input steps cycled through")
@@ -355,6 +402,9 @@ def main():
                          "soft cross-entropy draft loss")
     ap.add_argument("--loss-rows", type=int, default=4096, help="rows (token positions) of the draft loss")
     ap.add_argument("--topk", type=int, default=256, help="teacher tokens kept by the draft loss")
+    ap.add_argument("--all", action="store_true",
+                    help="every workload and mode in turn, one JSON line each (per-config records)")
+    ap.add_argument("--jsonl", default=None, help="also append each JSON line to this file")
     ap.add_argument("--sweep", action="store_true",
                     help="greedy verify time against M_eff at H=5120, V=151936 (one JSON line per M)")
     args = ap.parse_args()
@@ -375,7 +425,22 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     if args.op == "fuse":
         return bench_fuse(args, wl)
-    mode = args.mode or wl.modes[0]
+    if args.all:
+        cases = [(c, m) for c, w in synth.WORKLOADS.items() for m in w.modes]
+    else:
+        cases = [(args.workload, args.mode or wl.modes[0])]
+    for cid, mode in cases:
+        line = bench_verify(args, synth.WORKLOADS[cid], mode)
+        print(json.dumps(line), flush=True)
+        if args.jsonl:
+            with open(args.jsonl, "a") as fh:
+                fh.write(json.dumps(line) + "\n")
+
+
+def bench_verify(args, wl, mode):
+    """One verify workload and mode: the timed loop, the JSON line as a dict."""
+    import torch
+    import mtp_draft_verification_amd as mv
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     code = mv.DTYPE_BF16 if wl.dtype == "bf16" else mv.DTYPE_F32
@@ -460,15 +525,9 @@ def main():
     value = positions / elapsed
     alg_bytes, alg_flops = algorithmic(wl, mode)
     kern_s = kern_ms / 1e3 / nlaunch
-    achieved = alg_bytes / kern_s / 1e9
     traffic = recorded_traffic(wl, mode)
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None if traffic is None else round(traffic / kern_s / 1e9, 1),
-                "kernel_us": round(kern_s * 1e6, 2), "timed_launches": nlaunch,
-                "algorithmic_bytes_per_launch": alg_bytes,
-                "mfma_tflops": round(alg_flops / kern_s / 1e12, 2),
-                "mfma_frac": round(alg_flops / kern_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    roofline = roofline_of(alg_bytes, alg_flops, kern_s, traffic)
+    roofline["timed_launches"] = nlaunch
     line = {
         "metric": "verified positions/s (accepted tokens/s alongside) at 1 GPU; % of HBM roofline",
         "value": round(value, 1),
@@ -501,7 +560,7 @@ def main():
         gpu = {"drafts": [d.cpu().numpy() for d in d_pool[:nc]],
                "a": alen[:nc].cpu().numpy(), "out": outt[:nc].cpu().numpy()}
         line["cpu_baseline"], line["parity_vs_oracle"] = cpu_baseline(wl, mode, W_store, args.cpu_budget, gpu)
-    print(json.dumps(line), flush=True)
+    return line
 
 
 if __name__ == "__main__":

@@ -4,6 +4,7 @@
 #include "mtpv.h"
 #include "mtpv_internal.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -343,25 +344,34 @@ int spec_verify_dual(const void* target_hidden, const void* draft_hidden, const 
 }
 
 // Workspace of mtp_input_fuse: the projection's LM-head workspace (its error word
-// first), then the fused rows [B, 2H] bf16.
-// The fc projection [2H -> H] runs on the LM-head kernels with W_fc as the head. It
-// has only H output rows, so on the tiled kernel K is split in 8 slices, one per XCD
-// (the slice of the fused rows is shared in that XCD's L2, every W_fc byte is read
-// once), the H rows in tiles so that slices x tiles fill the compute units; the
-// slices' raw products land in the workspace and a fixed-order sum writes out.
+// first), then the fused rows [2B, 2H] bf16 (hi parts, then lo parts), then the
+// projection's raw products [ks, 2B, H] fp32.
+// The fc projection [2H -> H] runs on the LM-head kernels with W_fc as the head over
+// the 2B fused rows; a fixed-order sum adds each request's hi and lo rows (and the K
+// slices). On the tiled kernel, which these shapes take beyond a few rows, there are
+// only H output rows, so K is split in 8 slices, one per XCD (the slice of the fused
+// rows is shared in that XCD's L2, every W_fc byte is read once), with the H rows in
+// tiles so that slices x position chunks x tiles fill whole rounds of the compute
+// units.
 static int fuse_plan(int B, int H, Plan* p, size_t* x_off, size_t* part_off, size_t* total) {
-    if (H < 8 || H > (1 << 19)) return MTPV_EINVAL;
-    const int st = make_plan(MTPV_MODE_GREEDY, B, 0, 2 * H, H, MTPV_BF16, p);
+    if (H < 8 || H > (1 << 19) || B < 1 || B > (1 << 19)) return MTPV_EINVAL;
+    const int st = make_plan(MTPV_MODE_GREEDY, 2 * B, 0, 2 * H, H, MTPV_BF16, p);
     if (st != MTPV_OK) return st;
-    if (p->kind == KIND_WIDE && p->MC == 1) {
+    if (p->kind == KIND_WIDE) {
+        constexpr int kCUs = 256;
         p->ks = 8;
-        const int s_min = (H + wide_rows() - 1) / wide_rows();
-        p->S = std::min(std::max(s_min, 256 / p->ks), (H + 15) / 16);
-        p->grid = p->S * p->ks;
+        const long long per_tile = (long long)p->ks * p->MC;  // workgroups per row tile
+        const long long s_min = (H + wide_rows() - 1) / wide_rows();
+        const long long s_max = std::max(s_min, (long long)(H + 15) / 16);
+        long long S = std::max(s_min, (kCUs + per_tile - 1) / per_tile);
+        const long long rounds = (S * per_tile + kCUs - 1) / kCUs;
+        S = std::min(s_max, std::max(S, rounds * kCUs / per_tile));
+        p->S = (int)S;
+        p->grid = (int)(S * per_tile);
     }
     *x_off = align_up(p->total, 256);
-    *part_off = align_up(*x_off + (size_t)B * 2 * H * 2, 256);
-    *total = *part_off + (p->ks > 1 ? align_up((size_t)p->ks * B * H * sizeof(float), 256) : 0);
+    *part_off = align_up(*x_off + (size_t)2 * B * 2 * H * 2, 256);
+    *total = *part_off + align_up((size_t)p->ks * 2 * B * H * sizeof(float), 256);
     return MTPV_OK;
 }
 
@@ -401,14 +411,14 @@ int mtp_input_fuse(const int32_t* tokens, const void* embed, const void* hidden,
     fa.eps = (float)eps;
     if (launch_fuse(fa, s) != hipSuccess) return MTPV_ELAUNCH;
     // the projection: fused rows in the place of hidden states, W_fc in the place of
-    // the head, the fp32 result through the logit output (or the K slices' products,
-    // then their sum); the error word is the fusion kernel's
+    // the head, the raw fp32 products of every row (and K slice) through the logit
+    // output, then their fixed-order sum; the error word is the fusion kernel's
     float* part = reinterpret_cast<float*>(base + part_off);
     st = launch_head(p, base + x_off, nullptr, W_fc, nullptr, (float)kLog2e,
                      reinterpret_cast<Partial*>(base + p.off_partials), reinterpret_cast<float*>(base + p.off_dlogit),
-                     p.ks > 1 ? part : out, nullptr, s);
-    if (st != MTPV_OK || p.ks == 1) return st;
-    return launch_ksum(part, out, p.ks, (size_t)B * H, s) == hipSuccess ? MTPV_OK : MTPV_ELAUNCH;
+                     part, nullptr, s);
+    if (st != MTPV_OK) return st;
+    return launch_ksum(part, out, p.ks, 2, (size_t)B * H, s) == hipSuccess ? MTPV_OK : MTPV_ELAUNCH;
 }
 
 int spec_draft_sample(const void* draft_hidden, const void* W_lm, int B, int kd, int depth0, int H, int V,

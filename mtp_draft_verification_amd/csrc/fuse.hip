@@ -9,8 +9,13 @@
 //
 // One workgroup per request row: 16-byte loads of both rows, fp32 sums of squares
 // (per-thread partials, then a fixed-order wave and workgroup reduction), then the
-// scaled values rounded to bf16 (round to nearest even), written as
-// x[b] = [n_e(E[tok]) | n_h(h)], n(v) = v / sqrt(mean(v^2) + eps) * g.
+// scaled values n(v) = v / sqrt(mean(v^2) + eps) * g in fp32. The projection's
+// operands are bf16, so each fp32 value x is carried as two bf16 numbers: hi =
+// bf16(x) (round to nearest even) and lo = bf16(x - hi) (x - hi is exact in fp32);
+// hi + lo is x to 2^-17 relative. The fused input is written as 2B rows,
+//   row b     = hi parts of [n_e(E[tok]) | n_h(h)],
+//   row B + b = lo parts,
+// and the fc sums the two rows' products (bf16 x bf16 products are exact in fp32).
 // A token outside [0, V) contributes a zero row; workgroup 0 sets the call's device
 // error word from all tokens (one writer, so it also clears stale bits).
 #include "mtpv.h"
@@ -41,16 +46,18 @@ __device__ __forceinline__ float sq8(u32x4_t v) {
     return s;
 }
 
-// 8 values of v scaled by r and the matching 8 weights of g, packed back to bf16
-__device__ __forceinline__ u32x4_t scale8(u32x4_t v, u32x4_t g, float r) {
-    u32x4_t o;
+// 8 values of v scaled by r and the matching 8 weights of g, as bf16 hi and lo parts
+__device__ __forceinline__ void scale8(u32x4_t v, u32x4_t g, float r, u32x4_t& hi, u32x4_t& lo) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const unsigned int lo = to_bf16(bf16_lo(v[i]) * r * bf16_lo(g[i]));
-        const unsigned int hi = to_bf16(bf16_hi(v[i]) * r * bf16_hi(g[i]));
-        o[i] = lo | (hi << 16);
+        const float a = bf16_lo(v[i]) * r * bf16_lo(g[i]);
+        const float b = bf16_hi(v[i]) * r * bf16_hi(g[i]);
+        const unsigned int ah = to_bf16(a), bh = to_bf16(b);
+        const unsigned int al = to_bf16(a - __uint_as_float(ah << 16));
+        const unsigned int bl = to_bf16(b - __uint_as_float(bh << 16));
+        hi[i] = ah | (bh << 16);
+        lo[i] = al | (bl << 16);
     }
-    return o;
 }
 
 __device__ __forceinline__ float block_sum(float v, float* sh) {
@@ -102,11 +109,17 @@ __global__ __launch_bounds__(256) void fuse_kernel(FuseArgs p) {
 
     const u32x4_t* ge = reinterpret_cast<const u32x4_t*>(p.g_e);
     const u32x4_t* gh = reinterpret_cast<const u32x4_t*>(p.g_h);
-    u32x4_t* x = reinterpret_cast<u32x4_t*>(p.x + (size_t)b * p.H * 4);
+    u32x4_t* xh = reinterpret_cast<u32x4_t*>(p.x + (size_t)b * p.H * 4);
+    u32x4_t* xl = reinterpret_cast<u32x4_t*>(p.x + (size_t)(p.B + b) * p.H * 4);
     for (int i = tid; i < nv; i += 256) {
         const u32x4_t ev = ok ? e[i] : zero;
-        x[i] = scale8(ev, ge[i], re);
-        x[nv + i] = scale8(h[i], gh[i], rh);
+        u32x4_t hi, lo;
+        scale8(ev, ge[i], re, hi, lo);
+        xh[i] = hi;
+        xl[i] = lo;
+        scale8(h[i], gh[i], rh, hi, lo);
+        xh[nv + i] = hi;
+        xl[nv + i] = lo;
     }
 }
 

@@ -56,7 +56,8 @@ struct Plan {
     size_t lds;      // dynamic LDS bytes of the LM-head kernel
     int grid;        // LM-head workgroups (1-D, XCD-aware ordering when MC > 1)
     int ks;          // wide kernel: K slices (1: whole K per tile; > 1: raw partial
-                     // products per slice into the spill, summed by launch_ksum)
+                     // products per slice into the spill, summed by launch_ksum; grid
+                     // = S * MC * ks, slice fastest)
     int NJ;          // inverse-CDF jobs (0 in greedy mode)
     int C;           // chunks per job in the residual passes
     int ntiles;      // 64-element tiles per vocabulary row
@@ -82,12 +83,13 @@ struct LmHeadArgs {
     int32_t* err;           // cleared by the first workgroup (NULL: left alone)
     int tiles;              // skinny kernel: 4-row tiles per wave
     int rotate;             // skinny / wide kernels: rotation of the K order per wave / workgroup
-    int ks;                 // wide kernel: K slices (> 1 needs MC == 1; spill = [ks, Meff, V])
+    int ks;                 // wide kernel: K slices (> 1: raw products per slice, spill = [ks, Meff, V])
 };
 
-// out[i] = sum over s < ks of part[s * n + i], in slice order (n % 4 == 0, 16-byte
-// aligned): the K slices of a split wide-kernel launch.
-hipError_t launch_ksum(const float* part, float* out, int ks, size_t n, hipStream_t stream);
+// out[i] = sum over h < halves of (sum over s < ks of part[(s * halves + h) * n + i]),
+// each sum in order (n % 4 == 0, 16-byte aligned): the K slices of a split wide-kernel
+// launch, and the hi and lo rows of the fused MTP input.
+hipError_t launch_ksum(const float* part, float* out, int ks, int halves, size_t n, hipStream_t stream);
 
 hipError_t launch_lmhead(const Plan& plan, const LmHeadArgs& args, hipStream_t stream);
 hipError_t launch_skinny(const Plan& plan, const LmHeadArgs& args, hipStream_t stream);
@@ -146,7 +148,7 @@ struct FuseArgs {
     const uint8_t* hidden;  // [B, H] bf16
     const uint8_t* g_e;     // [H] bf16
     const uint8_t* g_h;     // [H] bf16
-    uint8_t* x;             // [B, 2H] bf16 (output)
+    uint8_t* x;             // [2B, 2H] bf16 (output): hi parts in rows 0..B-1, lo parts in B..2B-1
     int32_t* err;           // device error word (written by workgroup 0)
     int B, H, V;
     float eps;

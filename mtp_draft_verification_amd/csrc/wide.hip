@@ -172,13 +172,14 @@ __global__ __launch_bounds__(512, 1) void wide_kernel(LmHeadArgs p) {
     const int S = p.S;  // vocabulary tiles (= partials per position)
 
     // workgroup -> (vocabulary tile, position chunk); the chunks of one tile share an XCD.
-    // With K split in ks slices (MC == 1), workgroup g takes slice g % ks of tile
-    // g / ks: with ks = 8 each XCD works on one slice of K.
+    // With K split in ks slices, workgroup g takes slice g % ks of position chunk
+    // (g / ks) % MC of tile g / (ks MC): with ks = 8 each XCD works on one slice of K.
     int vt, mt, ksl = 0;
     if (p.ks > 1) {
-        vt = blockIdx.x / p.ks;
-        ksl = blockIdx.x - vt * p.ks;
-        mt = 0;
+        const int rest = blockIdx.x / p.ks;
+        ksl = blockIdx.x - rest * p.ks;
+        mt = rest % p.MC;
+        vt = rest / p.MC;
     } else if (p.MC == 1) {
         vt = blockIdx.x;
         mt = 0;
@@ -507,28 +508,39 @@ size_t wide_lds_bytes(int bm) {
 namespace {
 
 __global__ __launch_bounds__(256) void ksum_kernel(const float4* __restrict__ part, float4* __restrict__ out, int ks,
-                                                   size_t n4) {
+                                                   int halves, size_t n4) {
     for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
-        float4 a = part[i];
-        for (int s = 1; s < ks; ++s) {
-            const float4 b = part[(size_t)s * n4 + i];
-            a.x += b.x;
-            a.y += b.y;
-            a.z += b.z;
-            a.w += b.w;
+        float4 o;
+        for (int h = 0; h < halves; ++h) {
+            float4 a = part[(size_t)h * n4 + i];
+            for (int s = 1; s < ks; ++s) {
+                const float4 b = part[((size_t)s * halves + h) * n4 + i];
+                a.x += b.x;
+                a.y += b.y;
+                a.z += b.z;
+                a.w += b.w;
+            }
+            if (h == 0) {
+                o = a;
+            } else {
+                o.x += a.x;
+                o.y += a.y;
+                o.z += a.z;
+                o.w += a.w;
+            }
         }
-        out[i] = a;
+        out[i] = o;
     }
 }
 
 }  // namespace
 
-hipError_t launch_ksum(const float* part, float* out, int ks, size_t n, hipStream_t stream) {
+hipError_t launch_ksum(const float* part, float* out, int ks, int halves, size_t n, hipStream_t stream) {
     const size_t n4 = n / 4;
     const unsigned int blocks = (unsigned int)std::min<size_t>((n4 + 255) / 256, 2048);
-    if (blocks == 0) return hipSuccess;
+    if (blocks == 0 || ks < 1 || halves < 1) return hipSuccess;
     hipLaunchKernelGGL(ksum_kernel, dim3(blocks), dim3(256), 0, stream, reinterpret_cast<const float4*>(part),
-                       reinterpret_cast<float4*>(out), ks, n4);
+                       reinterpret_cast<float4*>(out), ks, halves, n4);
     return hipGetLastError();
 }
 

@@ -116,8 +116,9 @@ def check_invariants(res, drafts, k):
         assert out[b, a[b]] >= 0
 
 
-def compare_outcomes(mode, res, ora, k):
-    """Returns (positions, excused, failing requests)."""
+def compare_outcomes(mode, res, ora, k, details=None):
+    """Returns (positions, excused, failing requests). With a list `details`, appends
+    (request, window, distance to the threshold) for every excused difference."""
     a_g, out_g = res["a"], res["out"]
     a_o, out_o = ora["a"], ora["out"]
     B = len(a_g)
@@ -126,21 +127,19 @@ def compare_outcomes(mode, res, ora, k):
         if a_g[b] == a_o[b] and np.array_equal(out_g[b], out_o[b]):
             continue
         j = int(min(a_g[b], a_o[b]))
-        if a_g[b] != a_o[b]:
-            if mode == "greedy":
-                ok = ora["top2_gap"][b, j] <= WINDOW
-            else:
-                pd, qd = ora["p_d"][b, j], ora["q_d"][b, j]
-                ratio = pd / qd if qd > 0 else np.inf
-                ok = abs(ora["u_acc"][b, j] - ratio) <= WINDOW
+        if mode == "greedy":
+            kind, dist = "argmax", float(ora["top2_gap"][b, j])
+        elif a_g[b] != a_o[b]:
+            pd, qd = ora["p_d"][b, j], ora["q_d"][b, j]
+            ratio = pd / qd if qd > 0 else np.inf
+            kind, dist = "accept", float(abs(ora["u_acc"][b, j] - ratio))
         else:
-            if mode == "greedy":
-                ok = ora["top2_gap"][b, j] <= WINDOW
-            else:
-                u = ora["u_res"][b]
-                ok = abs(u - ora["cdf_lo"][b]) <= WINDOW or abs(u - ora["cdf_hi"][b]) <= WINDOW
-        if ok:
+            u = ora["u_res"][b]
+            kind, dist = "cdf", float(min(abs(u - ora["cdf_lo"][b]), abs(u - ora["cdf_hi"][b])))
+        if dist <= WINDOW:
             excused += 1
+            if details is not None:
+                details.append((b, kind, dist))
         else:
             fails.append((b, int(a_g[b]), int(a_o[b]), out_g[b].tolist(), out_o[b].tolist()))
     return B * (k + 1), excused, fails
