@@ -65,7 +65,8 @@ typedef enum mtpv_status {
     MTPV_EDTYPE = -4,     /* dtype is neither MTPV_BF16 nor MTPV_F32                   */
     MTPV_ELAUNCH = -5,    /* a kernel launch failed                                    */
     MTPV_EDEVICE = -6,    /* HIP runtime error (no device, bad stream, copy failed)    */
-    MTPV_ENULL = -7       /* a required pointer is NULL                                */
+    MTPV_ENULL = -7,      /* a required pointer is NULL                                */
+    MTPV_ESCRATCH = -8    /* spec_verify_greedy_noalloc: shape beyond its scratch      */
 } mtpv_status;
 
 typedef enum mtpv_dtype { MTPV_BF16 = 0, MTPV_F32 = 1 } mtpv_dtype;
@@ -175,6 +176,25 @@ MTPV_API int spec_verify_sample(const void* target_hidden, const void* draft_hid
                        int32_t* accepted_len, int32_t* out_tokens,
                        void* workspace, size_t workspace_bytes,
                        const mtpv_debug* debug, void* stream);
+
+/*
+ * spec_verify_greedy for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation and outputs as spec_verify_greedy, with no workspace argument. Its
+ * scratch is a file-scope device array of MTPV_NOALLOC_SCRATCH_BYTES held by each
+ * GPU the library runs on until the process ends; the call allocates nothing and
+ * records no timing events. A shape whose workspace (mtpv_workspace_bytes(B, k, H,
+ * V, dtype, MTPV_MODE_GREEDY)) exceeds that size returns MTPV_ESCRATCH before
+ * anything is enqueued. Every call on one GPU shares that GPU's array: calls that
+ * overlap in time on one GPU (other streams, other host threads) race and must be
+ * ordered by the caller. device_error: NULL, or a device int32 that receives the
+ * call's device error word (MTPV_DEVERR_* bits; cleared by the call itself).
+ * Other arguments, layouts and errors as for spec_verify_greedy.
+ */
+#define MTPV_NOALLOC_SCRATCH_BYTES (16u << 20)
+MTPV_API int spec_verify_greedy_noalloc(const void* hidden, const void* W_lm, const int32_t* draft_tokens,
+                       int B, int k, int H, int V, int dtype,
+                       int32_t* accepted_len, int32_t* out_tokens, int32_t* device_error, void* stream);
 
 /*
  * Verification with a draft count per request ("dynamic draft length", named as

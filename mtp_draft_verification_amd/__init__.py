@@ -10,6 +10,7 @@ Calls (names as in the C ABI):
   spec_verify_sample(target_hidden, draft_hidden[B,k,H], W, drafts, temperature, seed, offset,
                      accepted_len, out_tokens, workspace)
   spec_draft_sample(draft_hidden[B,kd,H], W, temperature, seed, offset, depth0, draft_tokens[B,kd], workspace)
+  spec_verify_greedy_noalloc(hidden, W, drafts, accepted_len, out_tokens, device_error)  no workspace
   spec_verify_greedy_ragged / spec_verify_sample_ragged(..., draft_len[B], ...)  per-request draft counts
   spec_verify_dual(target_hidden, draft_hidden, W, drafts, draft_len, temperature, seed, offset,
                    accepted_len_greedy, out_tokens_greedy, accepted_len_sample, out_tokens_sample, workspace)
@@ -32,7 +33,8 @@ DEVERR_TOKEN_RANGE = 4
 LOSS_MAX_TOPK = 512
 
 STATUS = {0: "MTPV_OK", -1: "MTPV_EINVAL", -2: "MTPV_EALIGN", -3: "MTPV_EWORKSPACE", -4: "MTPV_EDTYPE",
-          -5: "MTPV_ELAUNCH", -6: "MTPV_EDEVICE", -7: "MTPV_ENULL"}
+          -5: "MTPV_ELAUNCH", -6: "MTPV_EDEVICE", -7: "MTPV_ENULL", -8: "MTPV_ESCRATCH"}
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class MtpvError(RuntimeError):
@@ -61,6 +63,7 @@ _SIGNATURES = {
     "spec_verify_sample": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _d, _u64, _u64, _vp, _vp, _vp, _sz,
                                 _vp, _vp]),
     "spec_draft_sample": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _d, _u64, _u64, _vp, _vp, _sz, _vp, _vp]),
+    "spec_verify_greedy_noalloc": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp]),
     "spec_verify_greedy_ragged": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _sz, _vp, _vp]),
     "spec_verify_sample_ragged": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _d, _u64, _u64, _vp, _vp,
                                        _vp, _sz, _vp, _vp]),
@@ -185,6 +188,19 @@ def spec_verify_sample(target_hidden, draft_hidden, W, drafts, temperature, seed
                                   int(offset) & (2**64 - 1), _ptr(accepted_len), _ptr(out_tokens),
                                   _ptr(workspace), workspace.numel(), _dbg(debug), _stream(stream))
     _check(st, "spec_verify_sample")
+
+
+def spec_verify_greedy_noalloc(hidden, W, drafts, accepted_len, out_tokens, device_error=None, stream=None):
+    """spec_verify_greedy without a workspace (the library's per-GPU scratch array; for
+    callers that cannot allocate). device_error: optional int32 device tensor [1]."""
+    B, k1, H = hidden.shape
+    V = W.shape[0]
+    for n, t in (("hidden", hidden), ("W", W), ("drafts", drafts)):
+        _contig(n, t)
+    st = lib().spec_verify_greedy_noalloc(_ptr(hidden), _ptr(W), _ptr(drafts), B, k1 - 1, H, V, _dtype_code(W),
+                                          _ptr(accepted_len), _ptr(out_tokens), _ptr(device_error),
+                                          _stream(stream))
+    _check(st, "spec_verify_greedy_noalloc")
 
 
 def spec_verify_greedy_ragged(hidden, W, drafts, draft_len, accepted_len, out_tokens, workspace, debug=None,

@@ -98,7 +98,8 @@ int check_debug(const Plan& plan, const mtpv_debug* dbg) {
 // The LM-head kernel of `plan` on rows xt (then xd) against w, with the timing
 // events around it when enabled.
 int launch_head(const Plan& plan, const void* xt, const void* xd, const void* w, const int32_t* drafts, float c2f,
-                Partial* partials, float* dlogit, float* spill, int32_t* err, hipStream_t stream) {
+                Partial* partials, float* dlogit, float* spill, int32_t* err, hipStream_t stream,
+                bool timed = true) {
     LmHeadArgs la;
     la.xt = static_cast<const uint8_t*>(xt);
     la.xd = static_cast<const uint8_t*>(xd);
@@ -124,7 +125,7 @@ int launch_head(const Plan& plan, const void* xt, const void* xd, const void* w,
     la.rotate = plan.kind == KIND_WIDE ? 0 : k_rotate();
     la.ks = plan.kind == KIND_WIDE ? plan.ks : 1;
 
-    std::pair<hipEvent_t, hipEvent_t>* ev = timing_slot();
+    std::pair<hipEvent_t, hipEvent_t>* ev = timed ? timing_slot() : nullptr;
     if (ev && hipEventRecord(ev->first, stream) != hipSuccess) return MTPV_EDEVICE;
     const hipError_t le = plan.kind == KIND_SKINNY ? launch_skinny(plan, la, stream)
                           : plan.kind == KIND_WIDE ? launch_wide(plan, la, stream)
@@ -135,13 +136,15 @@ int launch_head(const Plan& plan, const void* xt, const void* xd, const void* w,
 }
 
 // One call: the LM-head launch, the decision pass (two passes for the dual call,
-// greedy first, into alen_g / out_g), and the sampling passes.
+// greedy first, into alen_g / out_g), and the sampling passes. err_word: where the
+// call's device error word goes (NULL: the workspace's own); timed: whether the
+// measurement hooks may record events around the LM-head launch.
 int run(const Plan& plan, const void* xt, const void* xd, const void* w, const int32_t* drafts,
         const int32_t* draft_len, double temperature, uint64_t seed, uint64_t offset, int depth0,
         int32_t* alen, int32_t* out, void* ws, const mtpv_debug* dbg, hipStream_t stream,
-        int32_t* alen_g = nullptr, int32_t* out_g = nullptr) {
+        int32_t* alen_g = nullptr, int32_t* out_g = nullptr, int32_t* err_word = nullptr, bool timed = true) {
     uint8_t* base = static_cast<uint8_t*>(ws);
-    int32_t* err = reinterpret_cast<int32_t*>(base + plan.off_err);
+    int32_t* err = err_word != nullptr ? err_word : reinterpret_cast<int32_t*>(base + plan.off_err);
     Partial* partials = reinterpret_cast<Partial*>(base + plan.off_partials);
     float* dlogit = reinterpret_cast<float*>(base + plan.off_dlogit);
     RowStat* rowstat = reinterpret_cast<RowStat*>(base + plan.off_rowstat);
@@ -156,7 +159,7 @@ int run(const Plan& plan, const void* xt, const void* xd, const void* w, const i
     const float c2f = (float)(kLog2e / T);
 
     const int hs = launch_head(plan, xt, xd, w, plan.mode == MTPV_MODE_DRAFT ? nullptr : drafts, c2f, partials,
-                               dlogit, spill, err, stream);
+                               dlogit, spill, err, stream, timed);
     if (hs != MTPV_OK) return hs;
 
     DecideArgs da;
@@ -224,6 +227,31 @@ int run(const Plan& plan, const void* xt, const void* xd, const void* w, const i
     return MTPV_OK;
 }
 
+// ------------------------------------------------ allocation-free entry point
+// spec_verify_greedy_noalloc keeps its workspace in this file-scope device array: one
+// copy per GPU, allocated with the code object and held until the process ends.
+// In host code the array's name is only a stand-in; the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and only that
+// address is ever handed to kernels.
+constexpr size_t kScratchBytes = MTPV_NOALLOC_SCRATCH_BYTES;
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of the scratch array, or nullptr (HIP error).
+void* scratch_address() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return nullptr;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (dev < kMaxDevices && g_scratch_ptr[dev] != nullptr) return g_scratch_ptr[dev];
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    if (dev < kMaxDevices) g_scratch_ptr[dev] = p;
+    return p;
+}
+
 }  // namespace
 
 bool timed_launch_events(hipEvent_t* start, hipEvent_t* stop) {
@@ -252,6 +280,7 @@ const char* mtpv_status_string(int status) {
         case MTPV_ENULL: return "required pointer is NULL";
         case MTPV_ELAUNCH: return "kernel launch failed";
         case MTPV_EDEVICE: return "HIP runtime error";
+        case MTPV_ESCRATCH: return "shape needs more workspace than the allocation-free call's scratch holds";
         default: return "unknown status";
     }
 }
@@ -432,6 +461,24 @@ int spec_draft_sample(const void* draft_hidden, const void* W_lm, int B, int kd,
     if (st != MTPV_OK) return st;
     return run(p, nullptr, draft_hidden, W_lm, draft_tokens, nullptr, temperature, seed, offset, depth0, nullptr,
                nullptr, workspace, debug, static_cast<hipStream_t>(stream));
+}
+
+int spec_verify_greedy_noalloc(const void* hidden, const void* W_lm, const int32_t* draft_tokens, int B, int k,
+                               int H, int V, int dtype, int32_t* accepted_len, int32_t* out_tokens,
+                               int32_t* device_error, void* stream) {
+    Plan p;
+    // the argument check of spec_verify_greedy, with a stand-in workspace of the
+    // scratch array's size (checked for size only, never used)
+    int st = common_check(MTPV_MODE_GREEDY, B, k, H, V, dtype, 1.0, hidden, nullptr, W_lm, draft_tokens,
+                          accepted_len, out_tokens, reinterpret_cast<const void*>((uintptr_t)256), kScratchBytes,
+                          &p);
+    if (st == MTPV_EWORKSPACE) return MTPV_ESCRATCH;  // the shape needs more than the scratch array
+    if (st != MTPV_OK) return st;
+    if (device_error != nullptr && !aligned(device_error, 4)) return MTPV_EALIGN;
+    void* ws = scratch_address();
+    if (ws == nullptr) return MTPV_EDEVICE;
+    return run(p, hidden, nullptr, W_lm, draft_tokens, nullptr, 1.0, 0, 0, 0, accepted_len, out_tokens, ws, nullptr,
+               static_cast<hipStream_t>(stream), nullptr, nullptr, device_error, false);
 }
 
 int mtpv_get_device_error(const void* workspace, int32_t* err, void* stream) {

@@ -228,7 +228,7 @@ def test_status_values_match_the_header():
     text = open(HEADER).read()
     decl = dict((n, int(v)) for n, v in re.findall(r"(MTPV_E?\w+)\s*=\s*(-?\d+)\s*[,}/]", text))
     want = {"MTPV_OK": 0, "MTPV_EINVAL": -1, "MTPV_EALIGN": -2, "MTPV_EWORKSPACE": -3, "MTPV_EDTYPE": -4,
-            "MTPV_ELAUNCH": -5, "MTPV_EDEVICE": -6, "MTPV_ENULL": -7}
+            "MTPV_ELAUNCH": -5, "MTPV_EDEVICE": -6, "MTPV_ENULL": -7, "MTPV_ESCRATCH": -8}
     for name, value in want.items():
         assert decl.get(name) == value, (name, decl.get(name))
         assert mv.STATUS[value] == name
@@ -245,3 +245,28 @@ def test_workspace_bytes_argument_order():
     assert s - g >= (B * (k + 1) + B * k) * V * 4
     assert L.mtpv_workspace_bytes(B, k, H, V, 0, 3) == 0   # no such mode
     assert L.mtpv_workspace_bytes(B, k, H, V, 2, 0) == 0   # no such dtype
+
+
+def test_noalloc_entry_point_rejects_before_touching_the_gpu():
+    """spec_verify_greedy_noalloc: argument errors and shapes beyond its scratch array
+    come back from the host check (nothing enqueued, no GPU needed)."""
+    L = mv.lib()
+    vp = ctypes.c_void_p
+    m = re.search(r"#define MTPV_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == mv.NOALLOC_SCRATCH_BYTES
+
+    def call(B=2, k=3, H=256, V=1000, dtype=0, hidden=A, W=A, drafts=A, alen=A, out=A, err=None):
+        return L.spec_verify_greedy_noalloc(vp(hidden), vp(W), vp(drafts), B, k, H, V, dtype, vp(alen), vp(out),
+                                            vp(err), None)
+
+    # 1024 requests x 4 rows of the 151936-token head: ~40 MB of partials > 16 MB
+    assert mv.workspace_bytes(1024, 3, 5120, 151936, 0, 0) > mv.NOALLOC_SCRATCH_BYTES
+    assert call(B=1024, k=3, H=5120, V=151936) == -8
+    assert mv.status_string(-8) != "unknown status"
+    assert call(W=None) == -7
+    assert call(hidden=None) == -7
+    assert call(H=12) == -2
+    assert call(hidden=A + 2) == -2
+    assert call(err=A + 2) == -2
+    assert call(B=0) == -1
+    assert call(dtype=7) == -4
