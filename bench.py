@@ -52,7 +52,8 @@ def log(*a):
 
 
 # Paths relative to the kernel sources; the build script sets the compiler flags.
-LMHEAD_SOURCES = ("lmhead.hip", "skinny.hip", "wide.hip", "mtpv_internal.h", "plan.hip", "../build.py")
+LMHEAD_SOURCES = ("lmhead.hip", "skinny.hip", "wide.hip", "headtile.hip", "mtpv_internal.h", "plan.hip",
+                  "../build.py")
 LOSS_SOURCES = ("loss.hip", "mtpv_internal.h", "../build.py")
 
 

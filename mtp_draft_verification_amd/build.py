@@ -21,7 +21,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmtpv.so")
 ARCH = os.environ.get("MTPV_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["api.hip", "plan.hip", "lmhead.hip", "skinny.hip", "wide.hip", "verify.hip", "fuse.hip", "loss.hip"]
+SOURCES = ["api.hip", "plan.hip", "lmhead.hip", "skinny.hip", "wide.hip", "headtile.hip", "verify.hip", "fuse.hip",
+           "loss.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",

@@ -127,9 +127,10 @@ int launch_head(const Plan& plan, const void* xt, const void* xd, const void* w,
 
     std::pair<hipEvent_t, hipEvent_t>* ev = timed ? timing_slot() : nullptr;
     if (ev && hipEventRecord(ev->first, stream) != hipSuccess) return MTPV_EDEVICE;
-    const hipError_t le = plan.kind == KIND_SKINNY ? launch_skinny(plan, la, stream)
-                          : plan.kind == KIND_WIDE ? launch_wide(plan, la, stream)
-                                                   : launch_lmhead(plan, la, stream);
+    const hipError_t le = plan.kind == KIND_SKINNY  ? launch_skinny(plan, la, stream)
+                          : plan.kind == KIND_HTILE ? launch_head_tile(plan, la, stream)
+                          : plan.kind == KIND_WIDE  ? launch_wide(plan, la, stream)
+                                                    : launch_lmhead(plan, la, stream);
     if (le != hipSuccess) return MTPV_ELAUNCH;
     if (ev && hipEventRecord(ev->second, stream) != hipSuccess) return MTPV_EDEVICE;
     return MTPV_OK;
@@ -384,7 +385,7 @@ int spec_verify_dual(const void* target_hidden, const void* draft_hidden, const 
 // units.
 static int fuse_plan(int B, int H, Plan* p, size_t* x_off, size_t* part_off, size_t* total) {
     if (H < 8 || H > (1 << 19) || B < 1 || B > (1 << 19)) return MTPV_EINVAL;
-    const int st = make_plan(MTPV_MODE_GREEDY, 2 * B, 0, 2 * H, H, MTPV_BF16, p);
+    const int st = make_plan(MTPV_MODE_GREEDY, 2 * B, 0, 2 * H, H, MTPV_BF16, p, KIND_WIDE);
     if (st != MTPV_OK) return st;
     if (p->kind == KIND_WIDE) {
         constexpr int kCUs = 256;

@@ -1,0 +1,519 @@
+// LM-head kernel for many positions (more than 16, bf16): batched verification,
+// the depth-5 chain and the large-batch rollout shape.
+//
+// The verify pass is a contraction l[m, v] = sum_h x[m, h] W[v, h] over every target
+// and drafter position m of the batch with the one head W ("The Tiny Draft Model
+// Hidden Inside Qwen", sections "One step deeper than the main model" and "How the
+// draft becomes real output"). With hundreds of positions the MFMA units, not HBM,
+// set the pace (same page: larger batches push the target from memory-bound toward
+// compute-bound), so it is an LDS-tiled matrix product laid out for gfx950:
+//
+//  * persistent: one workgroup of 4 waves per compute unit walks a list of items
+//    (vocabulary tile, position chunk). Workgroup w runs on XCD w % 8 and takes the
+//    items of the vocabulary tiles t = w % 8 (mod 8) in order, the position chunks of
+//    a tile next to each other: the workgroups of one XCD work on the chunks of the
+//    same tiles at the same time, so each W tile comes from HBM once and from that
+//    XCD's L2 for the other chunks;
+//  * a tile is at most 256 vocabulary rows (16 fragments of 16 rows) by at most 224
+//    positions (14 fragments), each split in two halves: wave w owns vocabulary half
+//    w % 2 (up to 128 rows) and position half w / 2 (up to 112 positions), 8 x 7
+//    accumulators of 16x16x32 bf16 MFMAs, one wave per SIMD. Per K-step a wave reads
+//    15 fragments from LDS for 56 MFMAs (a 64 x 128 wave tile would read 12 for 32);
+//  * both operands are staged in LDS in K-stages of 64 hidden elements (128 bytes per
+//    row) with 16-byte direct-to-LDS loads (one instruction = 8 whole 128-byte rows),
+//    3 stages of W and 2 of positions; 16-byte chunks XOR-swizzled by row so the
+//    fragment reads have no bank conflicts;
+//  * a wave whose position half ends early skips the padded fragments' reads and
+//    MFMAs (one instance of the stage loop per live-fragment count);
+//  * after the last stage each wave folds its logits into per-position statistics
+//    (max of l * c2, sum of exp2, argmax), gathers the draft logits and writes the fp32
+//    logits out when asked; the two vocabulary halves are merged in LDS into one
+//    partial per (position, vocabulary tile).
+// Accumulation is fp32 over all of H in a fixed order, no atomics.
+#include "mtpv_internal.h"
+
+#include <algorithm>
+#include <atomic>
+#include <climits>
+#include <type_traits>
+
+namespace mtpv {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int NT = 256;         // threads per workgroup (4 waves)
+constexpr int BK = 64;          // hidden elements per stage
+constexpr int ROWB = BK * 2;    // LDS bytes per staged row
+constexpr int CPR = BK / 8;     // 16-byte chunks per staged row
+constexpr int RPI = 64 / CPR;   // rows filled by one load instruction
+constexpr int VH = 128;         // vocabulary rows per half tile
+constexpr int BV = 2 * VH;      // vocabulary rows per tile
+constexpr int MH = 112;         // positions per half chunk
+constexpr int BM = 2 * MH;      // positions per chunk
+constexpr int FV = VH / 16;     // vocabulary fragments per wave
+constexpr int FM = MH / 16;     // position fragments per wave
+constexpr int WSTAGE = BV * ROWB;
+constexpr int XSTAGE = BM * ROWB;
+constexpr int NSW = 3;          // W stages
+constexpr int NSX = 2;          // position stages
+constexpr int LPW_W = BV / RPI / (NT / 64);  // W load instructions per wave per stage
+constexpr int LPW_X = BM / RPI / (NT / 64);  // position load instructions per wave per stage
+constexpr int STATS = 2 * BM * 16;           // per-half statistics of a chunk
+constexpr int PF_OFF = NSW * WSTAGE + NSX * XSTAGE + STATS;  // landing zone of the L2 prefetches
+constexpr int LDS = PF_OFF + 1024;
+static_assert(LDS <= 160 * 1024, "LDS");
+constexpr int PF_DIST = 5;  // L2 prefetch distance, in stages
+static_assert(LPW_W * RPI * (NT / 64) == BV && LPW_X * RPI * (NT / 64) == BM, "whole instructions");
+// The prologue issues W(0), X(0), W(1), X(1), W(2); phase 2 of iteration i issues
+// X(i + NSX) then W(i + NSW) (and, with prefetching, one prefetch after them). WAIT:
+// loads issued after X(kb + 1) when iteration kb waits for stage kb + 1 (W(kb + 2),
+// plus the prefetch issued with it from iteration 1 on); PRO_WAIT: loads issued after
+// X(0).
+constexpr int WAIT = LPW_W;
+constexpr int PRO_WAIT = LPW_W + (NSX - 1) * (LPW_W + LPW_X);
+static_assert(NSW == NSX + 1 && PRO_WAIT < 64, "wait counts");
+
+// Sixteen zero bytes: the source of the hidden-state chunks past H in the last stage
+// when H is not a multiple of 64 (a direct-to-LDS load cannot zero-fill).
+__device__ __attribute__((aligned(16))) const unsigned int kZero16[4] = {0u, 0u, 0u, 0u};
+
+struct WStat {
+    float x, s, bv;
+    int bi;
+};
+
+__device__ __forceinline__ WStat merge_wstat(WStat a, WStat b) {
+    const float ninf = -__builtin_inff();
+    WStat o;
+    o.x = fmaxf(a.x, b.x);
+    const float sa = (a.x == ninf) ? 0.f : a.s * exp2f(a.x - o.x);
+    const float sb = (b.x == ninf) ? 0.f : b.s * exp2f(b.x - o.x);
+    o.s = sa + sb;
+    const bool take_b = (b.bv > a.bv) || (b.bv == a.bv && b.bi < a.bi);
+    o.bv = take_b ? b.bv : a.bv;
+    o.bi = take_b ? b.bi : a.bi;
+    return o;
+}
+
+// s_waitcnt with only the vector-memory count set (expcnt and lgkmcnt at their
+// maxima): gfx9 encoding, vmcnt split over bits 3:0 and 15:14.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier for the stage ring: waits for this wave's LDS reads (lgkmcnt(0))
+// and meets the other waves, but not for outstanding direct-to-LDS loads
+// (__syncthreads() would wait for all of them, draining the ring); the ring's own
+// vmcnt wait covers the stage about to be read. The empty asm statements keep the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void stage_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt at their maxima
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Chunk swizzle of staged row r: any 16 consecutive rows read at one chunk index land
+// on 16 distinct 16-byte bank groups (of a 256-byte bank row).
+__device__ __forceinline__ int chunk_swz(int r) { return (r / (16 / CPR)) % CPR; }
+
+// Calls f(std::integral_constant<int, n>) for the run-time n in [0, N].
+template <int N, typename F>
+__device__ __forceinline__ void with_live(int n, F&& f) {
+    if constexpr (N == 0) {
+        f(std::integral_constant<int, 0>{});
+    } else {
+        if (n == N)
+            f(std::integral_constant<int, N>{});
+        else
+            with_live<N - 1>(n, f);
+    }
+}
+
+// One K-step of a wave: acc[fv][fm] += A fragment fv x B fragment fm for the NL live
+// position fragments, with N other instructions (LDS fragment reads, direct-to-LDS
+// loads) spread evenly between the MFMAs: item i goes after MFMA (i + 1) 8 NL / (N + 1)
+// - 1, so the wave issues them while the matrix pipe works. The accumulators live in
+// AGPRs ("+a"): with 224 of them the compiler's own allocation moved them between
+// registers around every MFMA. The MFMAs are volatile asm, which keeps their order
+// against the memory instructions around them.
+template <int I, int END, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < END) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, END>(f);
+    }
+}
+
+template <int NL, int N, typename F>
+__device__ __forceinline__ void mma_step(f32x4_t (&acc)[FV][FM], const u32x4_t (&a)[FV],
+                                         const u32x4_t (&b)[NL > 0 ? NL : 1], F&& item) {
+    constexpr int T = FV * NL;  // MFMAs
+    if constexpr (T == 0) {
+        static_for<0, N>(item);
+    } else {
+        static_for<0, T>([&](auto t_tag) __attribute__((always_inline)) {
+            constexpr int t = decltype(t_tag)::value;
+            constexpr int fm = t / FV, fv = t % FV;
+            asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[fv][fm]) : "v"(a[fv]), "v"(b[fm]));
+            static_for<0, N>([&](auto i_tag) __attribute__((always_inline)) {
+                constexpr int i = decltype(i_tag)::value;
+                if constexpr ((i + 1) * T / (N + 1) == t) item(i_tag);
+            });
+        });
+    }
+}
+
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// NTW: each W tile is read by one workgroup only (one position chunk), so its loads
+// carry the non-temporal hint. PF: several chunks share each W tile and each chunk is
+// shared by several tiles of a round, so every workgroup brings its share of both into
+// L2 PF_DIST stages ahead (one 4-byte load per 128-byte line; the loads of the sharers
+// then hit L2 instead of all waiting on the same misses). HFULL: H % 64 == 0, no
+// stage reads past the end of a row.
+template <bool NTW, bool PF, bool HFULL>
+__global__ __launch_bounds__(NT, 1) void head_tile_kernel(LmHeadArgs p) {
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    uint8_t* wring = smem;                                     // NSW stages of BV rows
+    uint8_t* xring = smem + NSW * WSTAGE;                      // NSX stages of BM rows
+    WStat* stats = reinterpret_cast<WStat*>(smem + NSW * WSTAGE + NSX * XSTAGE);  // [2][BM]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS addresses in SGPRs
+    const int vh = wave & 1;   // vocabulary half of the tile
+    const int mh = wave >> 1;  // position half of the chunk
+    const int H = p.H, V = p.V, S = p.S, MC = p.MC, Meff = p.Meff;
+    const int G = (V + 15) / 16;          // 16-row vocabulary fragments
+    const int Mf = (Meff + 15) / 16;      // 16-row position fragments
+    const int nk = (H + BK - 1) / BK;
+    const size_t rowbytes = (size_t)H * 2;
+    if (blockIdx.x == 0 && tid == 0 && p.err != nullptr) *p.err = 0;
+
+    // this workgroup's items: XCD x = blockIdx.x % 8 owns tiles x, x + 8, ...; item j of
+    // the XCD is (tile x + 8 (j / MC), chunk j % MC); the XCD's workgroups take j = c,
+    // c + per_xcd, ...
+    const int x = blockIdx.x & 7;
+    const int c = blockIdx.x >> 3;
+    const int per_xcd = gridDim.x >> 3;
+    const int nvt_x = S > x ? (S - x + 7) / 8 : 0;
+    const int nx = nvt_x * MC;
+
+    const int lrow = lane & 15;
+    const int lgrp = lane >> 4;
+    const int lswz = chunk_swz(lrow);
+    const int frag_off0 = lrow * ROWB + ((lgrp ^ lswz) << 4);
+    const int frag_off1 = lrow * ROWB + ((((4 + lgrp) % CPR) ^ lswz) << 4);
+    const float ninf = -__builtin_inff();
+
+    for (int j = c; j < nx; j += per_xcd) {
+        const int vt = x + 8 * (j / MC);
+        const int mc = j - (j / MC) * MC;
+        // vocabulary rows: fragments [vf0, vf1) of the tile, halves of g0 and g1 fragments
+        const int vf0 = (int)((long long)vt * G / S), vf1 = (int)((long long)(vt + 1) * G / S);
+        const int g0 = (vf1 - vf0 + 1) / 2;
+        const int vlast = min(V, 16 * vf1) - 1;
+        const int vbase_h = 16 * vf0 + (vh ? 16 * g0 : 0);            // this wave's first row
+        const int vr = min(16 * (vh ? (vf1 - vf0) / 2 : g0), V - vbase_h);  // its valid rows (may be <= 0)
+        // positions: fragments [pf0, pf1) of the chunk, halves of h0 and h1 fragments
+        const int pf0 = (int)((long long)mc * Mf / MC), pf1 = (int)((long long)(mc + 1) * Mf / MC);
+        const int h0 = (pf1 - pf0 + 1) / 2;
+        const int plast = min(Meff, 16 * pf1) - 1;
+        const int pbase_h = 16 * pf0 + (mh ? 16 * h0 : 0);
+        const int nlive = mh ? (pf1 - pf0) / 2 : h0;               // live fragments of this wave
+
+        // stage loads: W instruction i of this wave fills staged rows 64 wave + 8 i ..
+        // + 7 (one vocabulary half per pair of waves), position instruction i fills
+        // rows 56 wave + 8 i .. + 7 (waves 0, 1: first half, 2, 3: second half). Lane l
+        // writes slot l % CPR of row 8 i + l / CPR of its block and fetches chunk
+        // (l % CPR) ^ swz(row); swz depends only on (4 i + 4 wave [positions] + l / 16) % 8.
+        // Rows past the valid ones re-read the last valid row (results ignored).
+        const int lr = lane / CPR, lc = lane % CPR;
+        const int w_v0 = 16 * vf0 + (wave >= 2 ? 16 * g0 : 0) + 64 * (wave & 1) + lr;   // row of instruction 0
+        const int x_m0 = 16 * pf0 + (wave >= 2 ? 16 * h0 : 0) + 56 * (wave & 1) + lr;
+        // load instruction i of the W (position) ring: the data of stage kd into the
+        // buffer of stage ks (they differ only past the last stage, where a free buffer
+        // takes a repeat of the last stage so that every phase issues the same loads)
+        auto load_w = [&](int kd, int ks, int i) __attribute__((always_inline)) {
+            uint8_t* dst = wring + (ks % NSW) * WSTAGE + wave * LPW_W * 1024;
+            const int chunk = lc ^ ((4 * i + (lane >> 4)) & 7);
+            const int k = kd * BK + 8 * chunk;
+            const uint8_t* row = p.w + (size_t)min(w_v0 + 8 * i, vlast) * rowbytes;
+            const uint8_t* src = (HFULL || k < H) ? row + (size_t)k * 2 : row;
+            __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + i * 1024), 16, 0, NTW ? 2 : 0);
+        };
+        auto load_x = [&](int kd, int ks, int i) __attribute__((always_inline)) {
+            uint8_t* dst = xring + (ks % NSX) * XSTAGE + wave * LPW_X * 1024;
+            const int chunk = lc ^ ((4 * i + 4 * wave + (lane >> 4)) & 7);
+            const int k = kd * BK + 8 * chunk;
+            const int m = min(x_m0 + 8 * i, plast);
+            const uint8_t* row = m < p.Mt ? p.xt + (size_t)m * rowbytes : p.xd + (size_t)(m - p.Mt) * rowbytes;
+            const uint8_t* src = (HFULL || k < H) ? row + (size_t)k * 2 : reinterpret_cast<const uint8_t*>(kZero16);
+            __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + i * 1024), 16, 0, 0);
+        };
+        // prefetch shares: rows [wlo, whi) of the W tile (1 / MC of them, by chunk) and
+        // rows [xlo, xhi) of the position chunk (1 / nsh of them, nsh = items of a round
+        // with this chunk, by the tile's place in the round); one 128-byte line of each
+        // row per stage, spread over the lanes of the four waves
+        const int nrows_t = min(V, 16 * vf1) - 16 * vf0;
+        const int wlo = nrows_t * mc / MC, whi = nrows_t * (mc + 1) / MC;
+        const int nsh = max(1, per_xcd / MC);
+        const int tr = (j / MC) % nsh;
+        const int nrows_c = plast + 1 - 16 * pf0;
+        const int xlo = nrows_c * tr / nsh, xhi = nrows_c * (tr + 1) / nsh;
+        auto prefetch = [&](int kd) __attribute__((always_inline)) {
+            const int q = wave * 64 + lane;
+            const int nw = whi - wlo;
+            const uint8_t* src;
+            if (q < nw) {
+                src = p.w + (size_t)(16 * vf0 + wlo + q) * rowbytes;
+            } else if (q < nw + (xhi - xlo)) {
+                const int m = 16 * pf0 + xlo + (q - nw);
+                src = m < p.Mt ? p.xt + (size_t)m * rowbytes : p.xd + (size_t)(m - p.Mt) * rowbytes;
+            } else {
+                src = p.w + (size_t)(16 * vf0) * rowbytes;
+            }
+            src += (size_t)kd * BK * 2;
+            __builtin_amdgcn_global_load_lds(src, (lds_void*)(smem + PF_OFF + wave * 256), 4, 0, 0);
+        };
+        auto issue_w = [&](int kb) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < LPW_W; ++i) load_w(kb, kb, i);
+        };
+        auto issue_x = [&](int kb) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < LPW_X; ++i) load_x(kb, kb, i);
+        };
+        auto issue_mid = [&](int i) __attribute__((always_inline)) {
+            if (i + NSX >= 0 && i + NSX < nk) issue_x(i + NSX);
+            if (i + NSW >= 0 && i + NSW < nk) issue_w(i + NSW);
+        };
+
+        f32x4_t acc[FV][FM];
+#pragma unroll
+        for (int fv = 0; fv < FV; ++fv)
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) acc[fv][fm] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+        // Stage loop for NL live position fragments. Registers X hold the fragments of
+        // K-step 0 of stage kb, Y those of K-step 1. Phase 1: the MFMAs on X, with the
+        // reads of Y between them. Then this wave's loads of stage kb + 1 are waited for
+        // and the workgroup meets (every wave has read stage kb and holds it in
+        // registers). Phase 2: the MFMAs on Y, with the loads of later stages into
+        // stage kb's buffers and the reads of X for stage kb + 1 between them. Each
+        // phase ends with lgkmcnt(0), so the next phase's operands are complete.
+        auto stage_loop = [&](auto nl_tag) __attribute__((always_inline)) {
+            constexpr int NL = decltype(nl_tag)::value;
+            constexpr int NB = NL > 0 ? NL : 1;
+            constexpr int NR = FV + NL;  // fragment reads of one K-step
+            auto rd = [&](int kb, int s, u32x4_t (&a)[FV], u32x4_t (&b)[NB], auto i_tag) {
+                constexpr int i = decltype(i_tag)::value;
+                const int fo = s == 0 ? frag_off0 : frag_off1;
+                if constexpr (i < FV) {
+                    a[i] = *(const u32x4_t*)(wring + (kb % NSW) * WSTAGE + (vh * VH + i * 16) * ROWB + fo);
+                } else if constexpr (i - FV < NL) {
+                    b[i - FV] = *(const u32x4_t*)(xring + (kb % NSX) * XSTAGE + (mh * MH + (i - FV) * 16) * ROWB + fo);
+                }
+            };
+#pragma unroll
+            for (int i = -NSW; i < 0; ++i) issue_mid(i);
+            if (nk >= NSW) wait_vm<PRO_WAIT>();
+            else wait_vm<0>();
+            stage_barrier();  // stage 0 landed in every wave
+            u32x4_t a0[FV], b0[NB], a1[FV], b1[NB];
+            static_for<0, NR>([&](auto i) __attribute__((always_inline)) { rd(0, 0, a0, b0, i); });
+            wait_lgkm0();
+            for (int kb = 0; kb < nk; ++kb) {
+                mma_step<NL, NR>(acc, a0, b0, [&](auto i) __attribute__((always_inline)) { rd(kb, 1, a1, b1, i); });
+                wait_lgkm0();
+                if (kb + 1 < nk) {
+                    // this wave's loads of stage kb + 1 are done when only later ones remain:
+                    // after X(kb + 1) come W(kb + 2) (issued by the prologue or by phase 2 of
+                    // iteration kb - 1, always) and, from iteration 1 on, that phase's prefetch
+                    if (kb == 0 && NSW - 1 >= nk) wait_vm<0>();
+                    else if (PF && kb >= 1) wait_vm<WAIT + 1>();
+                    else wait_vm<WAIT>();
+                }
+                // stage kb + 1 landed everywhere, and every wave holds stage kb in registers,
+                // so its buffers may be refilled (also after the last stage: the repeat loads
+                // below must not land while another wave still reads them)
+                stage_barrier();
+                // Every phase 2 issues the same loads (past the last stage, repeats of the last
+                // stage into buffers no longer read), so the wait counts above hold; after the
+                // last stage the reads below fetch stale LDS, never used.
+                const int kx = min(kb + NSX, nk - 1), kw = min(kb + NSW, nk - 1);
+                mma_step<NL, LPW_X + LPW_W + NR>(acc, a1, b1, [&](auto i_tag) __attribute__((always_inline)) {
+                    constexpr int i = decltype(i_tag)::value;
+                    if constexpr (i < LPW_X) {
+                        load_x(kx, kb + NSX, i);
+                    } else if constexpr (i < LPW_X + LPW_W) {
+                        load_w(kw, kb + NSW, i - LPW_X);
+                        if constexpr (PF && i == LPW_X + LPW_W - 1) prefetch(min(kb + PF_DIST, nk - 1));
+                    } else {
+                        rd(kb + 1, 0, a0, b0, std::integral_constant<int, i - LPW_X - LPW_W>{});
+                    }
+                });
+                wait_lgkm0();
+            }
+            // the accumulators are read by VALU instructions next: wait out the last
+            // MFMAs (the compiler does not see inside the asm)
+            asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+        };
+        with_live<FM>(nlive, stage_loop);
+
+        // ------------------------------------------------------------- epilogue
+        const float c2 = p.c2;
+        const bool vec_spill = (V & 3) == 0;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int pl = mh * MH + 16 * fm + lrow;          // staged position row
+            const int pos = pbase_h + 16 * fm + lrow;
+            const bool pv = fm < nlive && pos <= plast;
+            float mx = ninf, bv = ninf;
+            int bi = INT_MAX;
+#pragma unroll
+            for (int fv = 0; fv < FV; ++fv)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int vo = 16 * fv + 4 * lgrp + t;
+                    const float l = acc[fv][fm][t];
+                    if (vo < vr) {
+                        mx = fmaxf(mx, l * c2);
+                        if (l > bv) {
+                            bv = l;
+                            bi = vbase_h + vo;
+                        }
+                    }
+                }
+#pragma unroll
+            for (int off = 16; off <= 32; off <<= 1) {
+                mx = fmaxf(mx, __shfl_xor(mx, off));
+                const float obv = __shfl_xor(bv, off);
+                const int obi = __shfl_xor(bi, off);
+                if (obv > bv || (obv == bv && obi < bi)) {
+                    bv = obv;
+                    bi = obi;
+                }
+            }
+            float s = 0.f;
+            if (mx != ninf) {
+#pragma unroll
+                for (int fv = 0; fv < FV; ++fv)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        if (16 * fv + 4 * lgrp + t < vr) s += exp2f(acc[fv][fm][t] * c2 - mx);
+            }
+            s += __shfl_xor(s, 16);
+            s += __shfl_xor(s, 32);
+            if (pv) {
+                // draft id of this position: slot j < k of a target row, or a drafter row
+                int d = -1;
+                if (p.drafts != nullptr) {
+                    if (pos < p.Mt) {
+                        const int b = pos / (p.k + 1);
+                        const int jj = pos - b * (p.k + 1);
+                        if (jj < p.k) d = p.drafts[b * p.k + jj];
+                    } else {
+                        d = p.drafts[pos - p.Mt];
+                    }
+                }
+                const int dd = d - vbase_h;
+                if (dd >= 0 && dd < vr && ((dd >> 2) & 3) == lgrp) {
+                    // the element without a run-time index into the accumulators
+                    const int fsel = dd >> 4, t = dd & 3;
+                    float l = 0.f;
+#pragma unroll
+                    for (int f = 0; f < FV; ++f) {
+                        const f32x4_t a = acc[f][fm];
+                        const float e = t == 0 ? a[0] : t == 1 ? a[1] : t == 2 ? a[2] : a[3];
+                        l = (f == fsel) ? e : l;
+                    }
+                    p.dlogit[pos] = l;
+                }
+                if (p.spill != nullptr) {
+#pragma unroll
+                    for (int fv = 0; fv < FV; ++fv) {
+                        const int vo = 16 * fv + 4 * lgrp;
+                        if (vo < vr) {
+                            float* dst = p.spill + (size_t)pos * V + vbase_h + vo;
+                            if (vec_spill && vo + 3 < vr) {
+                                *(f32x4_t*)dst = acc[fv][fm];
+                            } else {
+#pragma unroll
+                                for (int t = 0; t < 4; ++t)
+                                    if (vo + t < vr) dst[t] = acc[fv][fm][t];
+                            }
+                        }
+                    }
+                }
+            }
+            if (lgrp == 0) stats[vh * BM + pl] = WStat{mx, s, bv, bi};
+            __builtin_amdgcn_sched_barrier(0);  // one fragment's temporaries at a time
+        }
+        // the statistics are in LDS: a barrier on LDS only, so the spill stores keep
+        // draining while the workgroup goes on (__syncthreads() would wait for them)
+        stage_barrier();
+        // merge the two vocabulary halves: one partial per (position, tile)
+        if (tid < BM) {
+            const int hm = tid < MH ? 0 : 1;
+            const int r = tid - hm * MH;
+            const int pos = 16 * pf0 + (hm ? 16 * h0 : 0) + r;
+            const int live = hm ? (pf1 - pf0) / 2 : h0;
+            if (r < 16 * live && pos <= plast) {
+                const WStat o = merge_wstat(stats[tid], stats[BM + tid]);
+                p.partials[(size_t)pos * S + vt] = Partial{o.x, o.s, o.bv, o.bi};
+            }
+        }
+        stage_barrier();  // statistics read and every stage consumed: the next item may load
+    }
+}
+
+// Raises the kernel's dynamic-LDS limit, once per device.
+template <bool NTW, bool PF, bool HFULL>
+hipError_t allow_lds() {
+    static std::atomic<uint64_t> done{0};  // bit d: done on device d (devices past 63: every call)
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = dev >= 0 && dev < 64 ? (1ull << dev) : 0ull;
+    if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+    e = hipFuncSetAttribute((const void*)head_tile_kernel<NTW, PF, HFULL>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            LDS);
+    if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
+
+template <bool NTW, bool PF, bool HFULL>
+hipError_t launch_t(const Plan& plan, const LmHeadArgs& args, hipStream_t stream) {
+    const hipError_t e = allow_lds<NTW, PF, HFULL>();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((head_tile_kernel<NTW, PF, HFULL>), dim3(plan.grid), dim3(NT), LDS, stream, args);
+    return hipGetLastError();
+}
+
+template <bool HFULL>
+hipError_t launch_h(const Plan& plan, const LmHeadArgs& args, hipStream_t stream) {
+    // one chunk per tile: W streams once (non-temporal); several: shared, prefetched
+    return plan.MC == 1 ? launch_t<true, false, HFULL>(plan, args, stream)
+                        : launch_t<false, true, HFULL>(plan, args, stream);
+}
+
+}  // namespace
+
+size_t head_tile_lds_bytes() { return LDS; }
+
+int head_tile_max_positions() { return BM; }
+
+hipError_t launch_head_tile(const Plan& plan, const LmHeadArgs& args, hipStream_t stream) {
+    if (plan.grid % 8 != 0 || plan.grid < 8) return hipErrorInvalidConfiguration;
+    return plan.H % BK == 0 ? launch_h<true>(plan, args, stream) : launch_h<false>(plan, args, stream);
+}
+
+}  // namespace mtpv

@@ -39,7 +39,7 @@ struct Job {
     double ref_q;
 };
 
-enum { KIND_TILE = 0, KIND_SKINNY = 1, KIND_WIDE = 2 };
+enum { KIND_TILE = 0, KIND_SKINNY = 1, KIND_WIDE = 2, KIND_HTILE = 3 };
 
 struct Plan {
     int mode, B, k, H, V, dtype;
@@ -51,7 +51,7 @@ struct Plan {
     int S;           // vocab blocks (wide kernel: tiles, V split evenly, at most 256 rows each)
     int MC;          // M chunks
     int kc;          // hidden elements staged per LDS pass
-    int kind;        // LM-head kernel: KIND_SKINNY, KIND_WIDE or KIND_TILE
+    int kind;        // LM-head kernel: KIND_SKINNY, KIND_HTILE, KIND_WIDE or KIND_TILE
     int tiles;       // skinny kernel: 4-row tiles per wave
     size_t lds;      // dynamic LDS bytes of the LM-head kernel
     int grid;        // LM-head workgroups (1-D, XCD-aware ordering when MC > 1)
@@ -66,8 +66,10 @@ struct Plan {
     size_t total;
 };
 
-// Returns 0 and fills *plan, or a negative status for an invalid shape.
-int make_plan(int mode, int B, int k, int H, int V, int dtype, Plan* plan);
+// Returns 0 and fills *plan, or a negative status for an invalid shape. many_kind: the
+// kernel for more positions than the streaming kernel holds, bf16 (KIND_HTILE; the
+// MTP input fusion's K-split projection asks for KIND_WIDE).
+int make_plan(int mode, int B, int k, int H, int V, int dtype, Plan* plan, int many_kind = KIND_HTILE);
 
 struct LmHeadArgs {
     const uint8_t* xt;      // target rows [Mt, H]
@@ -94,6 +96,8 @@ hipError_t launch_ksum(const float* part, float* out, int ks, int halves, size_t
 hipError_t launch_lmhead(const Plan& plan, const LmHeadArgs& args, hipStream_t stream);
 hipError_t launch_skinny(const Plan& plan, const LmHeadArgs& args, hipStream_t stream);
 hipError_t launch_wide(const Plan& plan, const LmHeadArgs& args, hipStream_t stream);
+hipError_t launch_head_tile(const Plan& plan, const LmHeadArgs& args, hipStream_t stream);
+int head_tile_max_positions();  // positions per chunk of the persistent tiled kernel
 size_t wide_lds_bytes(int bm);  // dynamic LDS of the wide kernel for bm (64, 128 or 256) positions per tile
 int wide_rows();                // most vocabulary rows per wide-kernel tile
 

@@ -5,6 +5,7 @@
 #include "mtpv_internal.h"
 
 #include <algorithm>
+#include <cstdlib>
 #include <cstring>
 
 namespace mtpv {
@@ -16,6 +17,16 @@ constexpr int kLdsBudget = 64 * 1024;   // staging budget per workgroup (two wor
 constexpr size_t kLdsPerCU = 160 * 1024; // LDS of one gfx950 compute unit
 constexpr int kCUs = 256;                // compute units of one MI355X
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// MTPV_WIDE_KERNEL=old selects the earlier tiled kernel for many positions (A/B
+// measurements only).
+bool wide_forced() {
+    static const bool f = [] {
+        const char* e = std::getenv("MTPV_WIDE_KERNEL");
+        return e != nullptr && std::strcmp(e, "old") == 0;
+    }();
+    return f;
+}
 
 int shape_status(int mode, int B, int k, int H, int V, int dtype) {
     if (dtype != MTPV_BF16 && dtype != MTPV_F32) return MTPV_EDTYPE;
@@ -34,7 +45,7 @@ int shape_status(int mode, int B, int k, int H, int V, int dtype) {
 
 }  // namespace
 
-int make_plan(int mode, int B, int k, int H, int V, int dtype, Plan* pl) {
+int make_plan(int mode, int B, int k, int H, int V, int dtype, Plan* pl, int many_kind) {
     const int st = shape_status(mode, B, k, H, V, dtype);
     if (st != MTPV_OK) return st;
     Plan p;
@@ -82,7 +93,30 @@ int make_plan(int mode, int B, int k, int H, int V, int dtype, Plan* pl) {
             p.kc = H;
         }
     }
-    if (p.kind != KIND_SKINNY && p.es == 2) {
+    if (many_kind == KIND_HTILE && !wide_forced() && p.kind != KIND_SKINNY && p.es == 2) {
+        // Many positions, bf16: the persistent tiled kernel. Position chunks of at most
+        // 14 fragments (224 positions), split evenly; vocabulary tiles of at most 16
+        // fragments (256 rows), as many as make whole rounds of items over the compute
+        // units (tile edges on 16-row boundaries, every tile at least one fragment).
+        p.kind = KIND_HTILE;
+        const int cap = head_tile_max_positions() / 16;
+        const long long Mf = (p.Meff + 15) / 16;
+        p.MC = (int)((Mf + cap - 1) / cap);
+        const long long G = (V + 15) / 16;
+        const long long nvt_min = (G + 15) / 16;
+        const long long rounds = (nvt_min * p.MC + kCUs - 1) / kCUs;
+        long long S = std::max(nvt_min, rounds * kCUs / p.MC);
+        S = std::min(S, G);
+        p.S = (int)S;
+        const long long items = S * p.MC;
+        p.grid = (int)std::min<long long>(kCUs, (items + 7) / 8 * 8);
+        p.nt = head_tile_max_positions();
+        p.kc = 64;
+        p.lds = 0;
+        p.vblock = 0;
+        p.va = 0;
+    }
+    if (p.kind != KIND_SKINNY && p.kind != KIND_HTILE && p.es == 2) {
         // Many positions, bf16: LDS-tiled matrix product, one workgroup per tile of at
         // most 256 vocabulary rows by 64, 128 or 256 positions (whichever pads fewer
         // rows; 256 on a tie, so W is re-read from L2 fewer times), the position
