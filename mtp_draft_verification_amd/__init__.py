@@ -23,7 +23,8 @@ import ctypes
 import os
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG_DIR, "libmtpv.so")
+# MTPV_LIBRARY: another build of the library (measurements of variants); default in-tree
+LIB_PATH = os.environ.get("MTPV_LIBRARY") or os.path.join(PKG_DIR, "libmtpv.so")
 
 MODE_GREEDY, MODE_SAMPLE, MODE_DRAFT = 0, 1, 2
 DTYPE_BF16, DTYPE_F32 = 0, 1
