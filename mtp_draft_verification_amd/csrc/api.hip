@@ -98,7 +98,7 @@ int check_debug(const Plan& plan, const mtpv_debug* dbg) {
 // The LM-head kernel of `plan` on rows xt (then xd) against w, with the timing
 // events around it when enabled.
 int launch_head(const Plan& plan, const void* xt, const void* xd, const void* w, const int32_t* drafts, float c2f,
-                Partial* partials, float* dlogit, float* spill, int32_t* err, hipStream_t stream,
+                Partial* partials, float* dlogit, float* spill, int32_t* err, float* tail, hipStream_t stream,
                 bool timed = true) {
     LmHeadArgs la;
     la.xt = static_cast<const uint8_t*>(xt);
@@ -124,6 +124,11 @@ int launch_head(const Plan& plan, const void* xt, const void* xd, const void* w,
     // share their hidden-state and W chunks in L2.
     la.rotate = plan.kind == KIND_WIDE ? 0 : k_rotate();
     la.ks = plan.kind == KIND_WIDE ? plan.ks : 1;
+    la.tail = tail;
+    la.tail_f = plan.tail_f;
+    la.tail_r = plan.tail_r;
+    la.tail_ks = plan.tail_ks;
+    la.tail_fm = plan.tail_fm;
 
     std::pair<hipEvent_t, hipEvent_t>* ev = timed ? timing_slot() : nullptr;
     if (ev && hipEventRecord(ev->first, stream) != hipSuccess) return MTPV_EDEVICE;
@@ -159,8 +164,9 @@ int run(const Plan& plan, const void* xt, const void* xd, const void* w, const i
     const double T = plan.mode == MTPV_MODE_GREEDY ? 1.0 : temperature;
     const float c2f = (float)(kLog2e / T);
 
+    float* tail = reinterpret_cast<float*>(base + plan.off_tail);
     const int hs = launch_head(plan, xt, xd, w, plan.mode == MTPV_MODE_DRAFT ? nullptr : drafts, c2f, partials,
-                               dlogit, spill, err, stream, timed);
+                               dlogit, spill, err, tail, stream, timed);
     if (hs != MTPV_OK) return hs;
 
     DecideArgs da;
@@ -446,7 +452,7 @@ int mtp_input_fuse(const int32_t* tokens, const void* embed, const void* hidden,
     float* part = reinterpret_cast<float*>(base + part_off);
     st = launch_head(p, base + x_off, nullptr, W_fc, nullptr, (float)kLog2e,
                      reinterpret_cast<Partial*>(base + p.off_partials), reinterpret_cast<float*>(base + p.off_dlogit),
-                     part, nullptr, s);
+                     part, nullptr, nullptr, s);
     if (st != MTPV_OK) return st;
     return launch_ksum(part, out, p.ks, 2, (size_t)B * H, s) == hipSuccess ? MTPV_OK : MTPV_ELAUNCH;
 }

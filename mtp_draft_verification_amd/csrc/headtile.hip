@@ -172,12 +172,179 @@ __device__ __forceinline__ void mma_step(f32x4_t (&acc)[FV][FM], const u32x4_t (
 
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
+// Where an item's rows are: vocabulary fragments [vf0, vf1) of tile vt (halves of g0
+// and vf1 - vf0 - g0 fragments), position fragments [pf0, pf1) of chunk mc (halves of
+// h0 and pf1 - pf0 - h0), and this wave's share (vocabulary half vh, position half mh).
+struct Item {
+    int vt, vf0, vf1, g0, vlast, vbase_h, vr;
+    int pf0, pf1, h0, plast, pbase_h, nlive;
+};
+
+__device__ __forceinline__ Item item_at(const LmHeadArgs& p, int vt, int mc, int vh, int mh) {
+    const int G = (p.V + 15) / 16;
+    const int Mf = (p.Meff + 15) / 16;
+    Item t;
+    t.vt = vt;
+    t.vf0 = (int)((long long)vt * G / p.S);
+    t.vf1 = (int)((long long)(vt + 1) * G / p.S);
+    t.g0 = (t.vf1 - t.vf0 + 1) / 2;
+    t.vlast = min(p.V, 16 * t.vf1) - 1;
+    t.vbase_h = 16 * t.vf0 + (vh ? 16 * t.g0 : 0);                               // this wave's first row
+    t.vr = min(16 * (vh ? (t.vf1 - t.vf0) / 2 : t.g0), p.V - t.vbase_h);  // its valid rows (may be <= 0)
+    t.pf0 = (int)((long long)mc * Mf / p.MC);
+    t.pf1 = (int)((long long)(mc + 1) * Mf / p.MC);
+    t.h0 = (t.pf1 - t.pf0 + 1) / 2;
+    t.plast = min(p.Meff, 16 * t.pf1) - 1;
+    t.pbase_h = 16 * t.pf0 + (mh ? 16 * t.h0 : 0);
+    t.nlive = mh ? (t.pf1 - t.pf0) / 2 : t.h0;  // live position fragments of this wave
+    return t;
+}
+
+// One position fragment fm of a wave's share of an item (accumulators a[fv] = rows
+// 16 fv + 4 (lane / 16) .. + 3 of the wave's vocabulary half, positions 16 fm + lane % 16
+// of its position half): the statistics of each position over those rows (max of
+// l * c2, sum of exp2, argmax, combined across the four lane groups), the draft logits
+// gathered and the fp32 logits written out when asked. Returns the statistics (valid in
+// every lane; the caller keeps those of lane group 0).
+__device__ __forceinline__ WStat frag_stats(const LmHeadArgs& p, const Item& t, const f32x4_t (&a)[FV], int fm,
+                                            int lrow, int lgrp) {
+    const float ninf = -__builtin_inff();
+    const float c2 = p.c2;
+    const int V = p.V;
+    const bool vec_spill = (V & 3) == 0;
+    const int pos = t.pbase_h + 16 * fm + lrow;
+    const bool pv = fm < t.nlive && pos <= t.plast;
+    float mx = ninf, bv = ninf;
+    int bi = INT_MAX;
+#pragma unroll
+    for (int fv = 0; fv < FV; ++fv)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int vo = 16 * fv + 4 * lgrp + q;
+            const float l = a[fv][q];
+            if (vo < t.vr) {
+                mx = fmaxf(mx, l * c2);
+                if (l > bv) {
+                    bv = l;
+                    bi = t.vbase_h + vo;
+                }
+            }
+        }
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {
+        mx = fmaxf(mx, __shfl_xor(mx, off));
+        const float obv = __shfl_xor(bv, off);
+        const int obi = __shfl_xor(bi, off);
+        if (obv > bv || (obv == bv && obi < bi)) {
+            bv = obv;
+            bi = obi;
+        }
+    }
+    float s = 0.f;
+    if (mx != ninf) {
+#pragma unroll
+        for (int fv = 0; fv < FV; ++fv)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (16 * fv + 4 * lgrp + q < t.vr) s += exp2f(a[fv][q] * c2 - mx);
+    }
+    s += __shfl_xor(s, 16);
+    s += __shfl_xor(s, 32);
+    if (pv) {
+        // draft id of this position: slot j < k of a target row, or a drafter row
+        int d = -1;
+        if (p.drafts != nullptr) {
+            if (pos < p.Mt) {
+                const int b = pos / (p.k + 1);
+                const int jj = pos - b * (p.k + 1);
+                if (jj < p.k) d = p.drafts[b * p.k + jj];
+            } else {
+                d = p.drafts[pos - p.Mt];
+            }
+        }
+        const int dd = d - t.vbase_h;
+        if (dd >= 0 && dd < t.vr && ((dd >> 2) & 3) == lgrp) {
+            // the element without a run-time index into the accumulators
+            const int fsel = dd >> 4, q = dd & 3;
+            float l = 0.f;
+#pragma unroll
+            for (int f = 0; f < FV; ++f) {
+                const f32x4_t v = a[f];
+                const float e = q == 0 ? v[0] : q == 1 ? v[1] : q == 2 ? v[2] : v[3];
+                l = (f == fsel) ? e : l;
+            }
+            p.dlogit[pos] = l;
+        }
+        if (p.spill != nullptr) {
+#pragma unroll
+            for (int fv = 0; fv < FV; ++fv) {
+                const int vo = 16 * fv + 4 * lgrp;
+                if (vo < t.vr) {
+                    float* dst = p.spill + (size_t)pos * V + t.vbase_h + vo;
+                    if (vec_spill && vo + 3 < t.vr) {
+                        *(f32x4_t*)dst = a[fv];
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            if (vo + q < t.vr) dst[q] = a[fv][q];
+                    }
+                }
+            }
+        }
+    }
+    return WStat{mx, s, bv, bi};
+}
+
+// After the last stage of an item: every position fragment of each wave through
+// frag_stats, then the two vocabulary halves merged in LDS into one partial per
+// (position, vocabulary tile). Ends with the workgroup's LDS barrier.
+__device__ __forceinline__ void epilogue(const LmHeadArgs& p, const Item& t, f32x4_t (&acc)[FV][FM], WStat* stats,
+                                         int tid, int vh, int mh) {
+    const int lane = tid & 63;
+    const int lrow = lane & 15;
+    const int lgrp = lane >> 4;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+        f32x4_t a[FV];
+#pragma unroll
+        for (int fv = 0; fv < FV; ++fv) a[fv] = acc[fv][fm];
+        const WStat w = frag_stats(p, t, a, fm, lrow, lgrp);
+        if (lgrp == 0) stats[vh * BM + mh * MH + 16 * fm + lrow] = w;
+        __builtin_amdgcn_sched_barrier(0);  // one fragment's temporaries at a time
+    }
+    // the statistics are in LDS: a barrier on LDS only, so the spill stores keep
+    // draining while the workgroup goes on (__syncthreads() would wait for them)
+    stage_barrier();
+    // merge the two vocabulary halves: one partial per (position, tile)
+    if (tid < BM) {
+        const int hm = tid < MH ? 0 : 1;
+        const int r = tid - hm * MH;
+        const int pos = 16 * t.pf0 + (hm ? 16 * t.h0 : 0) + r;
+        const int live = hm ? (t.pf1 - t.pf0) / 2 : t.h0;
+        if (r < 16 * live && pos <= t.plast) {
+            const WStat o = merge_wstat(stats[tid], stats[BM + tid]);
+            p.partials[(size_t)pos * p.S + t.vt] = Partial{o.x, o.s, o.bv, o.bi};
+        }
+    }
+    stage_barrier();  // statistics read: the next item may write them
+}
+
+// Raw accumulators of one K piece of a split tile with fl live position fragments per
+// wave: register (fv, fm < fl) of thread tid at float4 (fv * fl + fm) * NT + tid of the
+// piece (each store instruction writes 4 KB in a row).
+__device__ __forceinline__ size_t piece_float4(int fl) { return (size_t)FV * fl * NT; }
+
 // NTW: each W tile is read by one workgroup only (one position chunk), so its loads
 // carry the non-temporal hint. PF: several chunks share each W tile and each chunk is
 // shared by several tiles of a round, so every workgroup brings its share of both into
 // L2 PF_DIST stages ahead (one 4-byte load per 128-byte line; the loads of the sharers
 // then hit L2 instead of all waiting on the same misses). HFULL: H % 64 == 0, no
 // stage reads past the end of a row.
+//
+// Items: the whole-K items of tiles [0, S') (S' = tail_f when tiles are split, else
+// S), then, when tiles are split, workgroup q < tail_r * tail_ks takes K piece q /
+// tail_r of tile tail_f + q % tail_r: the stages [piece * nk / ks, (piece + 1) * nk /
+// ks), whose raw accumulators go to p.tail for head_tile_tail_kernel.
 template <bool NTW, bool PF, bool HFULL>
 __global__ __launch_bounds__(NT, 1) void head_tile_kernel(LmHeadArgs p) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
@@ -190,20 +357,19 @@ __global__ __launch_bounds__(NT, 1) void head_tile_kernel(LmHeadArgs p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS addresses in SGPRs
     const int vh = wave & 1;   // vocabulary half of the tile
     const int mh = wave >> 1;  // position half of the chunk
-    const int H = p.H, V = p.V, S = p.S, MC = p.MC, Meff = p.Meff;
-    const int G = (V + 15) / 16;          // 16-row vocabulary fragments
-    const int Mf = (Meff + 15) / 16;      // 16-row position fragments
+    const int H = p.H, MC = p.MC;
     const int nk = (H + BK - 1) / BK;
     const size_t rowbytes = (size_t)H * 2;
     if (blockIdx.x == 0 && tid == 0 && p.err != nullptr) *p.err = 0;
 
-    // this workgroup's items: XCD x = blockIdx.x % 8 owns tiles x, x + 8, ...; item j of
-    // the XCD is (tile x + 8 (j / MC), chunk j % MC); the XCD's workgroups take j = c,
-    // c + per_xcd, ...
+    // this workgroup's whole-K items: XCD x = blockIdx.x % 8 owns tiles x, x + 8, ...;
+    // item j of the XCD is (tile x + 8 (j / MC), chunk j % MC); the XCD's workgroups
+    // take j = c, c + per_xcd, ...
     const int x = blockIdx.x & 7;
     const int c = blockIdx.x >> 3;
     const int per_xcd = gridDim.x >> 3;
-    const int nvt_x = S > x ? (S - x + 7) / 8 : 0;
+    const int S_whole = p.tail_r > 0 ? p.tail_f : p.S;
+    const int nvt_x = S_whole > x ? (S_whole - x + 7) / 8 : 0;
     const int nx = nvt_x * MC;
 
     const int lrow = lane & 15;
@@ -211,23 +377,13 @@ __global__ __launch_bounds__(NT, 1) void head_tile_kernel(LmHeadArgs p) {
     const int lswz = chunk_swz(lrow);
     const int frag_off0 = lrow * ROWB + ((lgrp ^ lswz) << 4);
     const int frag_off1 = lrow * ROWB + ((((4 + lgrp) % CPR) ^ lswz) << 4);
-    const float ninf = -__builtin_inff();
 
-    for (int j = c; j < nx; j += per_xcd) {
-        const int vt = x + 8 * (j / MC);
-        const int mc = j - (j / MC) * MC;
-        // vocabulary rows: fragments [vf0, vf1) of the tile, halves of g0 and g1 fragments
-        const int vf0 = (int)((long long)vt * G / S), vf1 = (int)((long long)(vt + 1) * G / S);
-        const int g0 = (vf1 - vf0 + 1) / 2;
-        const int vlast = min(V, 16 * vf1) - 1;
-        const int vbase_h = 16 * vf0 + (vh ? 16 * g0 : 0);            // this wave's first row
-        const int vr = min(16 * (vh ? (vf1 - vf0) / 2 : g0), V - vbase_h);  // its valid rows (may be <= 0)
-        // positions: fragments [pf0, pf1) of the chunk, halves of h0 and h1 fragments
-        const int pf0 = (int)((long long)mc * Mf / MC), pf1 = (int)((long long)(mc + 1) * Mf / MC);
-        const int h0 = (pf1 - pf0 + 1) / 2;
-        const int plast = min(Meff, 16 * pf1) - 1;
-        const int pbase_h = 16 * pf0 + (mh ? 16 * h0 : 0);
-        const int nlive = mh ? (pf1 - pf0) / 2 : h0;               // live fragments of this wave
+    // one item: stages [k0, k0 + nki) of (tile vt, chunk mc); piece >= 0: a K piece of a
+    // split tile (raw accumulators out, no epilogue)
+    auto run_item = [&](int vt, int mc, int k0, int nki, int piece) __attribute__((always_inline)) {
+        const Item t = item_at(p, vt, mc, vh, mh);
+        const int vf0 = t.vf0, g0 = t.g0, vlast = t.vlast;
+        const int pf0 = t.pf0, h0 = t.h0, plast = t.plast;
 
         // stage loads: W instruction i of this wave fills staged rows 64 wave + 8 i ..
         // + 7 (one vocabulary half per pair of waves), position instruction i fills
@@ -238,13 +394,13 @@ __global__ __launch_bounds__(NT, 1) void head_tile_kernel(LmHeadArgs p) {
         const int lr = lane / CPR, lc = lane % CPR;
         const int w_v0 = 16 * vf0 + (wave >= 2 ? 16 * g0 : 0) + 64 * (wave & 1) + lr;   // row of instruction 0
         const int x_m0 = 16 * pf0 + (wave >= 2 ? 16 * h0 : 0) + 56 * (wave & 1) + lr;
-        // load instruction i of the W (position) ring: the data of stage kd into the
+        // load instruction i of the W (position) ring: the data of stage k0 + kd into the
         // buffer of stage ks (they differ only past the last stage, where a free buffer
         // takes a repeat of the last stage so that every phase issues the same loads)
         auto load_w = [&](int kd, int ks, int i) __attribute__((always_inline)) {
             uint8_t* dst = wring + (ks % NSW) * WSTAGE + wave * LPW_W * 1024;
             const int chunk = lc ^ ((4 * i + (lane >> 4)) & 7);
-            const int k = kd * BK + 8 * chunk;
+            const int k = (k0 + kd) * BK + 8 * chunk;
             const uint8_t* row = p.w + (size_t)min(w_v0 + 8 * i, vlast) * rowbytes;
             const uint8_t* src = (HFULL || k < H) ? row + (size_t)k * 2 : row;
             __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + i * 1024), 16, 0, NTW ? 2 : 0);
@@ -252,7 +408,7 @@ __global__ __launch_bounds__(NT, 1) void head_tile_kernel(LmHeadArgs p) {
         auto load_x = [&](int kd, int ks, int i) __attribute__((always_inline)) {
             uint8_t* dst = xring + (ks % NSX) * XSTAGE + wave * LPW_X * 1024;
             const int chunk = lc ^ ((4 * i + 4 * wave + (lane >> 4)) & 7);
-            const int k = kd * BK + 8 * chunk;
+            const int k = (k0 + kd) * BK + 8 * chunk;
             const int m = min(x_m0 + 8 * i, plast);
             const uint8_t* row = m < p.Mt ? p.xt + (size_t)m * rowbytes : p.xd + (size_t)(m - p.Mt) * rowbytes;
             const uint8_t* src = (HFULL || k < H) ? row + (size_t)k * 2 : reinterpret_cast<const uint8_t*>(kZero16);
@@ -262,10 +418,10 @@ __global__ __launch_bounds__(NT, 1) void head_tile_kernel(LmHeadArgs p) {
         // rows [xlo, xhi) of the position chunk (1 / nsh of them, nsh = items of a round
         // with this chunk, by the tile's place in the round); one 128-byte line of each
         // row per stage, spread over the lanes of the four waves
-        const int nrows_t = min(V, 16 * vf1) - 16 * vf0;
+        const int nrows_t = min(p.V, 16 * t.vf1) - 16 * vf0;
         const int wlo = nrows_t * mc / MC, whi = nrows_t * (mc + 1) / MC;
         const int nsh = max(1, per_xcd / MC);
-        const int tr = (j / MC) % nsh;
+        const int tr = (vt / 8) % nsh;
         const int nrows_c = plast + 1 - 16 * pf0;
         const int xlo = nrows_c * tr / nsh, xhi = nrows_c * (tr + 1) / nsh;
         auto prefetch = [&](int kd) __attribute__((always_inline)) {
@@ -280,7 +436,7 @@ __global__ __launch_bounds__(NT, 1) void head_tile_kernel(LmHeadArgs p) {
             } else {
                 src = p.w + (size_t)(16 * vf0) * rowbytes;
             }
-            src += (size_t)kd * BK * 2;
+            src += (size_t)(k0 + kd) * BK * 2;
             __builtin_amdgcn_global_load_lds(src, (lds_void*)(smem + PF_OFF + wave * 256), 4, 0, 0);
         };
         auto issue_w = [&](int kb) __attribute__((always_inline)) {
@@ -292,8 +448,8 @@ __global__ __launch_bounds__(NT, 1) void head_tile_kernel(LmHeadArgs p) {
             for (int i = 0; i < LPW_X; ++i) load_x(kb, kb, i);
         };
         auto issue_mid = [&](int i) __attribute__((always_inline)) {
-            if (i + NSX >= 0 && i + NSX < nk) issue_x(i + NSX);
-            if (i + NSW >= 0 && i + NSW < nk) issue_w(i + NSW);
+            if (i + NSX >= 0 && i + NSX < nki) issue_x(i + NSX);
+            if (i + NSW >= 0 && i + NSW < nki) issue_w(i + NSW);
         };
 
         f32x4_t acc[FV][FM];
@@ -324,20 +480,20 @@ __global__ __launch_bounds__(NT, 1) void head_tile_kernel(LmHeadArgs p) {
             };
 #pragma unroll
             for (int i = -NSW; i < 0; ++i) issue_mid(i);
-            if (nk >= NSW) wait_vm<PRO_WAIT>();
+            if (nki >= NSW) wait_vm<PRO_WAIT>();
             else wait_vm<0>();
             stage_barrier();  // stage 0 landed in every wave
             u32x4_t a0[FV], b0[NB], a1[FV], b1[NB];
             static_for<0, NR>([&](auto i) __attribute__((always_inline)) { rd(0, 0, a0, b0, i); });
             wait_lgkm0();
-            for (int kb = 0; kb < nk; ++kb) {
+            for (int kb = 0; kb < nki; ++kb) {
                 mma_step<NL, NR>(acc, a0, b0, [&](auto i) __attribute__((always_inline)) { rd(kb, 1, a1, b1, i); });
                 wait_lgkm0();
-                if (kb + 1 < nk) {
+                if (kb + 1 < nki) {
                     // this wave's loads of stage kb + 1 are done when only later ones remain:
                     // after X(kb + 1) come W(kb + 2) (issued by the prologue or by phase 2 of
                     // iteration kb - 1, always) and, from iteration 1 on, that phase's prefetch
-                    if (kb == 0 && NSW - 1 >= nk) wait_vm<0>();
+                    if (kb == 0 && NSW - 1 >= nki) wait_vm<0>();
                     else if (PF && kb >= 1) wait_vm<WAIT + 1>();
                     else wait_vm<WAIT>();
                 }
@@ -348,14 +504,14 @@ __global__ __launch_bounds__(NT, 1) void head_tile_kernel(LmHeadArgs p) {
                 // Every phase 2 issues the same loads (past the last stage, repeats of the last
                 // stage into buffers no longer read), so the wait counts above hold; after the
                 // last stage the reads below fetch stale LDS, never used.
-                const int kx = min(kb + NSX, nk - 1), kw = min(kb + NSW, nk - 1);
+                const int kx = min(kb + NSX, nki - 1), kw = min(kb + NSW, nki - 1);
                 mma_step<NL, LPW_X + LPW_W + NR>(acc, a1, b1, [&](auto i_tag) __attribute__((always_inline)) {
                     constexpr int i = decltype(i_tag)::value;
                     if constexpr (i < LPW_X) {
                         load_x(kx, kb + NSX, i);
                     } else if constexpr (i < LPW_X + LPW_W) {
                         load_w(kw, kb + NSW, i - LPW_X);
-                        if constexpr (PF && i == LPW_X + LPW_W - 1) prefetch(min(kb + PF_DIST, nk - 1));
+                        if constexpr (PF && i == LPW_X + LPW_W - 1) prefetch(min(kb + PF_DIST, nki - 1));
                     } else {
                         rd(kb + 1, 0, a0, b0, std::integral_constant<int, i - LPW_X - LPW_W>{});
                     }
@@ -365,113 +521,81 @@ __global__ __launch_bounds__(NT, 1) void head_tile_kernel(LmHeadArgs p) {
             // the accumulators are read by VALU instructions next: wait out the last
             // MFMAs (the compiler does not see inside the asm)
             asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-        };
-        with_live<FM>(nlive, stage_loop);
-
-        // ------------------------------------------------------------- epilogue
-        const float c2 = p.c2;
-        const bool vec_spill = (V & 3) == 0;
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-            const int pl = mh * MH + 16 * fm + lrow;          // staged position row
-            const int pos = pbase_h + 16 * fm + lrow;
-            const bool pv = fm < nlive && pos <= plast;
-            float mx = ninf, bv = ninf;
-            int bi = INT_MAX;
-#pragma unroll
-            for (int fv = 0; fv < FV; ++fv)
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int vo = 16 * fv + 4 * lgrp + t;
-                    const float l = acc[fv][fm][t];
-                    if (vo < vr) {
-                        mx = fmaxf(mx, l * c2);
-                        if (l > bv) {
-                            bv = l;
-                            bi = vbase_h + vo;
-                        }
-                    }
-                }
-#pragma unroll
-            for (int off = 16; off <= 32; off <<= 1) {
-                mx = fmaxf(mx, __shfl_xor(mx, off));
-                const float obv = __shfl_xor(bv, off);
-                const int obi = __shfl_xor(bi, off);
-                if (obv > bv || (obv == bv && obi < bi)) {
-                    bv = obv;
-                    bi = obi;
-                }
-            }
-            float s = 0.f;
-            if (mx != ninf) {
+            if (piece >= 0) {
+                // a K piece: this wave's live accumulators out
+                f32x4_t* dst = reinterpret_cast<f32x4_t*>(p.tail) + (size_t)piece * piece_float4(p.tail_fm) + tid;
+                const int fl = p.tail_fm;
 #pragma unroll
                 for (int fv = 0; fv < FV; ++fv)
 #pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        if (16 * fv + 4 * lgrp + t < vr) s += exp2f(acc[fv][fm][t] * c2 - mx);
+                    for (int fm = 0; fm < NL; ++fm) dst[(fv * fl + fm) * NT] = acc[fv][fm];
             }
-            s += __shfl_xor(s, 16);
-            s += __shfl_xor(s, 32);
-            if (pv) {
-                // draft id of this position: slot j < k of a target row, or a drafter row
-                int d = -1;
-                if (p.drafts != nullptr) {
-                    if (pos < p.Mt) {
-                        const int b = pos / (p.k + 1);
-                        const int jj = pos - b * (p.k + 1);
-                        if (jj < p.k) d = p.drafts[b * p.k + jj];
-                    } else {
-                        d = p.drafts[pos - p.Mt];
-                    }
-                }
-                const int dd = d - vbase_h;
-                if (dd >= 0 && dd < vr && ((dd >> 2) & 3) == lgrp) {
-                    // the element without a run-time index into the accumulators
-                    const int fsel = dd >> 4, t = dd & 3;
-                    float l = 0.f;
+        };
+        with_live<FM>(t.nlive, stage_loop);
+
+        if (piece < 0) epilogue(p, t, acc, stats, tid, vh, mh);
+        else stage_barrier();  // every wave is past its stage loop
+    };
+
+    for (int j = c; j < nx; j += per_xcd) run_item(x + 8 * (j / MC), j - (j / MC) * MC, 0, nk, -1);
+    if (p.tail_r > 0 && (int)blockIdx.x < p.tail_r * p.tail_ks) {
+        const int q = blockIdx.x;
+        const int kp = q / p.tail_r;
+        const int kbeg = (int)((long long)kp * nk / p.tail_ks), kend = (int)((long long)(kp + 1) * nk / p.tail_ks);
+        run_item(p.tail_f + q % p.tail_r, 0, kbeg, kend - kbeg, q);
+    }
+    // no direct-to-LDS load may still be landing when the workgroup's LDS is released
+    wait_vm<0>();
+}
+
+// Finishes the split tiles, one position fragment of one position half of a tile per
+// workgroup of two waves (the two vocabulary halves): workgroup ((u * 2 + mh) * FM + fm)
+// takes tile tail_f + u. Each thread adds, in piece order, the raw accumulators that the
+// head kernel's thread (vh + 2 mh) * 64 + lane held for that fragment, runs frag_stats on
+// the sums and the halves are merged as in the head kernel's epilogue.
+__global__ __launch_bounds__(128) void head_tile_tail_kernel(LmHeadArgs p) {
+    __shared__ WStat stats[2][16];
+    const int u = blockIdx.x / (2 * FM);
+    const int mh = (blockIdx.x / FM) % 2;
+    const int fm = blockIdx.x % FM;
+    const int vh = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const Item t = item_at(p, p.tail_f + u, 0, vh, mh);
+    if (fm >= t.nlive) return;  // the same for both waves of the workgroup
+    const int tid = (vh + 2 * mh) * 64 + lane;
+    const int fl = p.tail_fm;
+    f32x4_t v[4][FV];
+    f32x4_t a[FV];
 #pragma unroll
-                    for (int f = 0; f < FV; ++f) {
-                        const f32x4_t a = acc[f][fm];
-                        const float e = t == 0 ? a[0] : t == 1 ? a[1] : t == 2 ? a[2] : a[3];
-                        l = (f == fsel) ? e : l;
-                    }
-                    p.dlogit[pos] = l;
-                }
-                if (p.spill != nullptr) {
+    for (int fv = 0; fv < FV; ++fv) a[fv] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < p.tail_ks; k0 += 4) {
+        // up to 4 pieces' loads in flight, then their sums in piece order
 #pragma unroll
-                    for (int fv = 0; fv < FV; ++fv) {
-                        const int vo = 16 * fv + 4 * lgrp;
-                        if (vo < vr) {
-                            float* dst = p.spill + (size_t)pos * V + vbase_h + vo;
-                            if (vec_spill && vo + 3 < vr) {
-                                *(f32x4_t*)dst = acc[fv][fm];
-                            } else {
+        for (int kq = 0; kq < 4; ++kq) {
+            if (k0 + kq < p.tail_ks) {
+                const f32x4_t* src = reinterpret_cast<const f32x4_t*>(p.tail) +
+                                     (size_t)(u + (k0 + kq) * p.tail_r) * piece_float4(fl) + fm * NT + tid;
 #pragma unroll
-                                for (int t = 0; t < 4; ++t)
-                                    if (vo + t < vr) dst[t] = acc[fv][fm][t];
-                            }
-                        }
-                    }
-                }
-            }
-            if (lgrp == 0) stats[vh * BM + pl] = WStat{mx, s, bv, bi};
-            __builtin_amdgcn_sched_barrier(0);  // one fragment's temporaries at a time
-        }
-        // the statistics are in LDS: a barrier on LDS only, so the spill stores keep
-        // draining while the workgroup goes on (__syncthreads() would wait for them)
-        stage_barrier();
-        // merge the two vocabulary halves: one partial per (position, tile)
-        if (tid < BM) {
-            const int hm = tid < MH ? 0 : 1;
-            const int r = tid - hm * MH;
-            const int pos = 16 * pf0 + (hm ? 16 * h0 : 0) + r;
-            const int live = hm ? (pf1 - pf0) / 2 : h0;
-            if (r < 16 * live && pos <= plast) {
-                const WStat o = merge_wstat(stats[tid], stats[BM + tid]);
-                p.partials[(size_t)pos * S + vt] = Partial{o.x, o.s, o.bv, o.bi};
+                for (int fv = 0; fv < FV; ++fv) v[kq][fv] = src[(size_t)fv * fl * NT];
             }
         }
-        stage_barrier();  // statistics read and every stage consumed: the next item may load
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq)
+            if (k0 + kq < p.tail_ks) {
+#pragma unroll
+                for (int fv = 0; fv < FV; ++fv) a[fv] += v[kq][fv];
+            }
+    }
+    const WStat w = frag_stats(p, t, a, fm, lane & 15, lane >> 4);
+    if ((lane >> 4) == 0) stats[vh][lane & 15] = w;
+    __syncthreads();
+    if (threadIdx.x < 16) {
+        const int r = threadIdx.x;
+        const int pos = t.pbase_h + 16 * fm + r;
+        if (pos <= t.plast) {
+            const WStat o = merge_wstat(stats[0][r], stats[1][r]);
+            p.partials[(size_t)pos * p.S + t.vt] = Partial{o.x, o.s, o.bv, o.bi};
+        }
     }
 }
 
@@ -495,6 +619,11 @@ hipError_t launch_t(const Plan& plan, const LmHeadArgs& args, hipStream_t stream
     const hipError_t e = allow_lds<NTW, PF, HFULL>();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((head_tile_kernel<NTW, PF, HFULL>), dim3(plan.grid), dim3(NT), LDS, stream, args);
+    if (args.tail_r > 0) {
+        const hipError_t le = hipGetLastError();
+        if (le != hipSuccess) return le;
+        hipLaunchKernelGGL(head_tile_tail_kernel, dim3(args.tail_r * 2 * FM), dim3(128), 0, stream, args);
+    }
     return hipGetLastError();
 }
 
@@ -511,8 +640,15 @@ size_t head_tile_lds_bytes() { return LDS; }
 
 int head_tile_max_positions() { return BM; }
 
+size_t head_tile_piece_bytes(int fm) { return (size_t)FV * fm * NT * 16; }
+
 hipError_t launch_head_tile(const Plan& plan, const LmHeadArgs& args, hipStream_t stream) {
     if (plan.grid % 8 != 0 || plan.grid < 8) return hipErrorInvalidConfiguration;
+    // split tiles: one chunk, every piece a workgroup of the grid, a non-empty K range each
+    if (args.tail_r > 0 && (plan.MC != 1 || args.tail == nullptr || args.tail_ks < 2 ||
+                            args.tail_r * args.tail_ks > plan.grid || args.tail_f + args.tail_r != plan.S ||
+                            args.tail_ks > (plan.H + BK - 1) / BK || args.tail_fm < 1 || args.tail_fm > FM))
+        return hipErrorInvalidConfiguration;
     return plan.H % BK == 0 ? launch_h<true>(plan, args, stream) : launch_h<false>(plan, args, stream);
 }
 

@@ -58,11 +58,14 @@ struct Plan {
     int ks;          // wide kernel: K slices (1: whole K per tile; > 1: raw partial
                      // products per slice into the spill, summed by launch_ksum; grid
                      // = S * MC * ks, slice fastest)
+    int tail_f, tail_r, tail_ks;  // tiled kernel, one position chunk: tiles [tail_f, tail_f + tail_r) are
+                                  // split along K in tail_ks pieces (0 tail tiles: none split)
+    int tail_fm;                  // live position fragments per wave of those tiles
     int NJ;          // inverse-CDF jobs (0 in greedy mode)
     int C;           // chunks per job in the residual passes
     int ntiles;      // 64-element tiles per vocabulary row
     // workspace layout (byte offsets)
-    size_t off_err, off_partials, off_dlogit, off_rowstat, off_jobs, off_zpart, off_tsum, off_spill;
+    size_t off_err, off_partials, off_dlogit, off_rowstat, off_jobs, off_zpart, off_tsum, off_spill, off_tail;
     size_t total;
 };
 
@@ -86,6 +89,8 @@ struct LmHeadArgs {
     int tiles;              // skinny kernel: 4-row tiles per wave
     int rotate;             // skinny / wide kernels: rotation of the K order per wave / workgroup
     int ks;                 // wide kernel: K slices (> 1: raw products per slice, spill = [ks, Meff, V])
+    float* tail;            // tiled kernel: raw accumulators of the K pieces of the split tiles
+    int tail_f, tail_r, tail_ks, tail_fm;
 };
 
 // out[i] = sum over h < halves of (sum over s < ks of part[(s * halves + h) * n + i]),
@@ -98,6 +103,7 @@ hipError_t launch_skinny(const Plan& plan, const LmHeadArgs& args, hipStream_t s
 hipError_t launch_wide(const Plan& plan, const LmHeadArgs& args, hipStream_t stream);
 hipError_t launch_head_tile(const Plan& plan, const LmHeadArgs& args, hipStream_t stream);
 int head_tile_max_positions();  // positions per chunk of the persistent tiled kernel
+size_t head_tile_piece_bytes(int fm);  // raw accumulators of one K piece of a split tile (fm live fragments)
 size_t wide_lds_bytes(int bm);  // dynamic LDS of the wide kernel for bm (64, 128 or 256) positions per tile
 int wide_rows();                // most vocabulary rows per wide-kernel tile
 

@@ -58,6 +58,7 @@ int make_plan(int mode, int B, int k, int H, int V, int dtype, Plan* pl, int man
     p.dtype = dtype;
     p.es = dtype == MTPV_BF16 ? 2 : 4;
     p.ks = 1;
+    p.tail_ks = 1;
     if (mode == MTPV_MODE_DRAFT) {
         p.Mt = 0;
         p.Meff = B * k;
@@ -107,6 +108,21 @@ int make_plan(int mode, int B, int k, int H, int V, int dtype, Plan* pl, int man
         const long long rounds = (nvt_min * p.MC + kCUs - 1) / kCUs;
         long long S = std::max(nvt_min, rounds * kCUs / p.MC);
         S = std::min(S, G);
+        // One position chunk and whole 256-row tiles that leave the last round part
+        // full: the whole rounds as they are, the tiles left over cut along K into
+        // pieces that fill the compute units instead (raw accumulators to the
+        // workspace, added in piece order by a second kernel that finishes those
+        // tiles). Padding the rounds with smaller tiles instead keeps the MFMA work of
+        // 256-row tiles for fewer live rows.
+        const long long full = nvt_min / kCUs * kCUs, left = nvt_min - full;
+        if (p.MC == 1 && full > 0 && left > 0 && kCUs / left >= 2) {
+            S = nvt_min;
+            p.tail_f = (int)full;
+            p.tail_r = (int)left;
+            p.tail_ks = (int)std::min<long long>(std::min<long long>(8, kCUs / left), (H + 63) / 64);
+            p.tail_fm = (int)((Mf + 1) / 2);
+            if (p.tail_ks < 2) p.tail_f = p.tail_r = p.tail_fm = 0, p.tail_ks = 1;
+        }
         p.S = (int)S;
         const long long items = S * p.MC;
         p.grid = (int)std::min<long long>(kCUs, (items + 7) / 8 * 8);
@@ -190,6 +206,8 @@ int make_plan(int mode, int B, int k, int H, int V, int dtype, Plan* pl, int man
     off = align_up(off + (size_t)p.NJ * p.ntiles * sizeof(double), 256);
     p.off_spill = off;
     if (mode != MTPV_MODE_GREEDY) off = align_up(off + (size_t)p.Meff * V * sizeof(float), 256);
+    p.off_tail = off;
+    off = align_up(off + (size_t)p.tail_r * p.tail_ks * head_tile_piece_bytes(p.tail_fm), 256);
     p.total = off;
     *pl = p;
     return MTPV_OK;
