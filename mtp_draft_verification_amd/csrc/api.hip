@@ -395,7 +395,10 @@ static int fuse_plan(int B, int H, Plan* p, size_t* x_off, size_t* part_off, siz
     if (st != MTPV_OK) return st;
     if (p->kind == KIND_WIDE) {
         constexpr int kCUs = 256;
-        p->ks = 8;
+        // K slices: 8 fill the compute units for few rows; with more than 256 rows (two
+        // position chunks) 4 do, and the slices' raw products in the workspace (written
+        // and read back once each) are half as many bytes
+        p->ks = 2 * B > 256 ? 4 : 8;
         const long long per_tile = (long long)p->ks * p->MC;  // workgroups per row tile
         const long long s_min = (H + wide_rows() - 1) / wide_rows();
         const long long s_max = std::max(s_min, (long long)(H + 15) / 16);
