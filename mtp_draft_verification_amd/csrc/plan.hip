@@ -94,7 +94,13 @@ int make_plan(int mode, int B, int k, int H, int V, int dtype, Plan* pl, int man
             p.kc = H;
         }
     }
-    if (many_kind == KIND_HTILE && !wide_forced() && p.kind != KIND_SKINNY && p.es == 2) {
+    // Up to 96 head rows the W stream sets the time and the wide kernel's one-tile
+    // workgroups keep more of it in flight (H = 5120, V = 151936 greedy: 242 against
+    // 277 us at 20 rows, 300 against 310 us at 96); from 112 rows on the tiled kernel
+    // is as fast or faster (326 against 342 us at 128, 350 against 404 us at 160).
+    constexpr int kWideMaxRows = 96;
+    if (many_kind == KIND_HTILE && !wide_forced() && p.kind != KIND_SKINNY && p.es == 2 &&
+        p.Meff > kWideMaxRows) {
         // Many positions, bf16: the persistent tiled kernel. Position chunks of at most
         // 14 fragments (224 positions), split evenly; vocabulary tiles of at most 16
         // fragments (256 rows), as many as make whole rounds of items over the compute
