@@ -50,32 +50,43 @@ constexpr int BK = 64;          // hidden elements per stage
 constexpr int ROWB = BK * 2;    // LDS bytes per staged row
 constexpr int CPR = BK / 8;     // 16-byte chunks per staged row
 constexpr int RPI = 64 / CPR;   // rows filled by one load instruction
-constexpr int VH = 128;         // vocabulary rows per half tile
-constexpr int BV = 2 * VH;      // vocabulary rows per tile
-constexpr int MH = 112;         // positions per half chunk
-constexpr int BM = 2 * MH;      // positions per chunk
-constexpr int FV = VH / 16;     // vocabulary fragments per wave
-constexpr int FM = MH / 16;     // position fragments per wave
-constexpr int WSTAGE = BV * ROWB;
-constexpr int XSTAGE = BM * ROWB;
-constexpr int NSW = 3;          // W stages
-constexpr int NSX = 2;          // position stages
-constexpr int LPW_W = BV / RPI / (NT / 64);  // W load instructions per wave per stage
-constexpr int LPW_X = BM / RPI / (NT / 64);  // position load instructions per wave per stage
-constexpr int STATS = 2 * BM * 16;           // per-half statistics of a chunk
-constexpr int PF_OFF = NSW * WSTAGE + NSX * XSTAGE + STATS;  // landing zone of the L2 prefetches
-constexpr int LDS = PF_OFF + 1024;
-static_assert(LDS <= 160 * 1024, "LDS");
-constexpr int PF_DIST = 5;  // L2 prefetch distance, in stages
-static_assert(LPW_W * RPI * (NT / 64) == BV && LPW_X * RPI * (NT / 64) == BM, "whole instructions");
-// The prologue issues W(0), X(0), W(1), X(1), W(2); phase 2 of iteration i issues
-// X(i + NSX) then W(i + NSW) (and, with prefetching, one prefetch after them). WAIT:
-// loads issued after X(kb + 1) when iteration kb waits for stage kb + 1 (W(kb + 2),
-// plus the prefetch issued with it from iteration 1 on); PRO_WAIT: loads issued after
-// X(0).
-constexpr int WAIT = LPW_W;
-constexpr int PRO_WAIT = LPW_W + (NSX - 1) * (LPW_W + LPW_X);
-static_assert(NSW == NSX + 1 && PRO_WAIT < 64, "wait counts");
+constexpr int PF_DIST = 5;     // L2 prefetch distance, in stages
+
+// Tile geometry: a wave holds FV x FM accumulator fragments (vocabulary x positions),
+// the workgroup's tile is 2 FV x 2 FM fragments, and the W ring has NSW stages (the
+// position ring 2). The prologue issues W(0) .. W(NSW - NSX - 1), then X(0), W(NSW -
+// NSX), X(1), W(NSW - 1); phase 2 of iteration i issues X(i + NSX) then W(i + NSW) (and,
+// with prefetching, one prefetch after them). WAIT: loads issued after X(kb + 1) when
+// iteration kb waits for stage kb + 1 (W(kb + NSW - 1), plus the prefetch issued with
+// it from iteration 1 on; W(kb + 1) came before X(kb + 1)); PRO_WAIT: loads issued
+// after X(0).
+template <int FV_, int FM_, int NSW_>
+struct Geo {
+    static constexpr int FV = FV_;           // vocabulary fragments per wave
+    static constexpr int FM = FM_;           // position fragments per wave
+    static constexpr int VH = 16 * FV;       // vocabulary rows per half tile
+    static constexpr int BV = 2 * VH;        // vocabulary rows per tile
+    static constexpr int MH = 16 * FM;       // positions per half chunk
+    static constexpr int BM = 2 * MH;        // positions per chunk
+    static constexpr int WSTAGE = BV * ROWB;
+    static constexpr int XSTAGE = BM * ROWB;
+    static constexpr int NSW = NSW_;         // W stages
+    static constexpr int NSX = 2;            // position stages
+    static constexpr int LPW_W = BV / RPI / (NT / 64);  // W load instructions per wave per stage
+    static constexpr int LPW_X = BM / RPI / (NT / 64);  // position load instructions per wave per stage
+    static constexpr int STATS = 2 * BM * 16;           // per-half statistics of a chunk
+    static constexpr int PF_OFF = NSW * WSTAGE + NSX * XSTAGE + STATS;  // landing zone of the L2 prefetches
+    static constexpr int LDS = PF_OFF + 1024;
+    static constexpr int WAIT = LPW_W;
+    static constexpr int PRO_WAIT = LPW_W + (NSX - 1) * (LPW_W + LPW_X);
+    static_assert(LDS <= 160 * 1024, "LDS");
+    static_assert(LPW_W * RPI * (NT / 64) == BV && LPW_X * RPI * (NT / 64) == BM, "whole instructions");
+    static_assert(NSW > NSX && PRO_WAIT < 64, "wait counts");
+};
+// 256 vocabulary rows x 224 positions, 3 W stages (152 KB); 192 x 128 with 5 W stages
+// (4 in flight, 152 KB) for at most 128 positions, where the W stream sets the pace
+using GeoL = Geo<8, 7, 3>;
+using GeoS = Geo<6, 4, 5>;
 
 // Sixteen zero bytes: the source of the hidden-state chunks past H in the last stage
 // when H is not a multiple of 64 (a direct-to-LDS load cannot zero-fill).
@@ -151,9 +162,10 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
-template <int NL, int N, typename F>
-__device__ __forceinline__ void mma_step(f32x4_t (&acc)[FV][FM], const u32x4_t (&a)[FV],
+template <class G, int NL, int N, typename F>
+__device__ __forceinline__ void mma_step(f32x4_t (&acc)[G::FV][G::FM], const u32x4_t (&a)[G::FV],
                                          const u32x4_t (&b)[NL > 0 ? NL : 1], F&& item) {
+    constexpr int FV = G::FV;
     constexpr int T = FV * NL;  // MFMAs
     if constexpr (T == 0) {
         static_for<0, N>(item);
@@ -206,8 +218,10 @@ __device__ __forceinline__ Item item_at(const LmHeadArgs& p, int vt, int mc, int
 // l * c2, sum of exp2, argmax, combined across the four lane groups), the draft logits
 // gathered and the fp32 logits written out when asked. Returns the statistics (valid in
 // every lane; the caller keeps those of lane group 0).
-__device__ __forceinline__ WStat frag_stats(const LmHeadArgs& p, const Item& t, const f32x4_t (&a)[FV], int fm,
+template <class G>
+__device__ __forceinline__ WStat frag_stats(const LmHeadArgs& p, const Item& t, const f32x4_t (&a)[G::FV], int fm,
                                             int lrow, int lgrp) {
+    constexpr int FV = G::FV;
     const float ninf = -__builtin_inff();
     const float c2 = p.c2;
     const int V = p.V;
@@ -298,8 +312,10 @@ __device__ __forceinline__ WStat frag_stats(const LmHeadArgs& p, const Item& t, 
 // After the last stage of an item: every position fragment of each wave through
 // frag_stats, then the two vocabulary halves merged in LDS into one partial per
 // (position, vocabulary tile). Ends with the workgroup's LDS barrier.
-__device__ __forceinline__ void epilogue(const LmHeadArgs& p, const Item& t, f32x4_t (&acc)[FV][FM], WStat* stats,
-                                         int tid, int vh, int mh) {
+template <class G>
+__device__ __forceinline__ void epilogue(const LmHeadArgs& p, const Item& t, f32x4_t (&acc)[G::FV][G::FM],
+                                         WStat* stats, int tid, int vh, int mh) {
+    constexpr int FV = G::FV, FM = G::FM, MH = G::MH, BM = G::BM;
     const int lane = tid & 63;
     const int lrow = lane & 15;
     const int lgrp = lane >> 4;
@@ -308,7 +324,7 @@ __device__ __forceinline__ void epilogue(const LmHeadArgs& p, const Item& t, f32
         f32x4_t a[FV];
 #pragma unroll
         for (int fv = 0; fv < FV; ++fv) a[fv] = acc[fv][fm];
-        const WStat w = frag_stats(p, t, a, fm, lrow, lgrp);
+        const WStat w = frag_stats<G>(p, t, a, fm, lrow, lgrp);
         if (lgrp == 0) stats[vh * BM + mh * MH + 16 * fm + lrow] = w;
         __builtin_amdgcn_sched_barrier(0);  // one fragment's temporaries at a time
     }
@@ -332,7 +348,8 @@ __device__ __forceinline__ void epilogue(const LmHeadArgs& p, const Item& t, f32
 // Raw accumulators of one K piece of a split tile with fl live position fragments per
 // wave: register (fv, fm < fl) of thread tid at float4 (fv * fl + fm) * NT + tid of the
 // piece (each store instruction writes 4 KB in a row).
-__device__ __forceinline__ size_t piece_float4(int fl) { return (size_t)FV * fl * NT; }
+template <class G>
+__device__ __forceinline__ size_t piece_float4(int fl) { return (size_t)G::FV * fl * NT; }
 
 // NTW: each W tile is read by one workgroup only (one position chunk), so its loads
 // carry the non-temporal hint. PF: several chunks share each W tile and each chunk is
@@ -345,8 +362,11 @@ __device__ __forceinline__ size_t piece_float4(int fl) { return (size_t)FV * fl 
 // S), then, when tiles are split, workgroup q < tail_r * tail_ks takes K piece q /
 // tail_r of tile tail_f + q % tail_r: the stages [piece * nk / ks, (piece + 1) * nk /
 // ks), whose raw accumulators go to p.tail for head_tile_tail_kernel.
-template <bool NTW, bool PF, bool HFULL>
+template <class G, bool NTW, bool PF, bool HFULL>
 __global__ __launch_bounds__(NT, 1) void head_tile_kernel(LmHeadArgs p) {
+    constexpr int FV = G::FV, FM = G::FM, VH = G::VH, MH = G::MH;
+    constexpr int WSTAGE = G::WSTAGE, XSTAGE = G::XSTAGE, NSW = G::NSW, NSX = G::NSX;
+    constexpr int LPW_W = G::LPW_W, LPW_X = G::LPW_X, PF_OFF = G::PF_OFF, WAIT = G::WAIT, PRO_WAIT = G::PRO_WAIT;
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     uint8_t* wring = smem;                                     // NSW stages of BV rows
     uint8_t* xring = smem + NSW * WSTAGE;                      // NSX stages of BM rows
@@ -385,21 +405,21 @@ __global__ __launch_bounds__(NT, 1) void head_tile_kernel(LmHeadArgs p) {
         const int vf0 = t.vf0, g0 = t.g0, vlast = t.vlast;
         const int pf0 = t.pf0, h0 = t.h0, plast = t.plast;
 
-        // stage loads: W instruction i of this wave fills staged rows 64 wave + 8 i ..
-        // + 7 (one vocabulary half per pair of waves), position instruction i fills
-        // rows 56 wave + 8 i .. + 7 (waves 0, 1: first half, 2, 3: second half). Lane l
-        // writes slot l % CPR of row 8 i + l / CPR of its block and fetches chunk
-        // (l % CPR) ^ swz(row); swz depends only on (4 i + 4 wave [positions] + l / 16) % 8.
+        // stage loads: W instruction i of this wave fills staged rows 8 LPW_W wave + 8 i
+        // .. + 7 (one vocabulary half per pair of waves), position instruction i fills
+        // rows 8 LPW_X wave + 8 i .. + 7 (waves 0, 1: first half, 2, 3: second half). Lane
+        // l writes slot l % CPR of row 8 i + l / CPR of its block and fetches chunk
+        // (l % CPR) ^ swz(row); swz(row) = (4 LPW wave + 4 i + l / 16) % 8.
         // Rows past the valid ones re-read the last valid row (results ignored).
         const int lr = lane / CPR, lc = lane % CPR;
-        const int w_v0 = 16 * vf0 + (wave >= 2 ? 16 * g0 : 0) + 64 * (wave & 1) + lr;   // row of instruction 0
-        const int x_m0 = 16 * pf0 + (wave >= 2 ? 16 * h0 : 0) + 56 * (wave & 1) + lr;
+        const int w_v0 = 16 * vf0 + (wave >= 2 ? 16 * g0 : 0) + 8 * LPW_W * (wave & 1) + lr;  // row of instruction 0
+        const int x_m0 = 16 * pf0 + (wave >= 2 ? 16 * h0 : 0) + 8 * LPW_X * (wave & 1) + lr;
         // load instruction i of the W (position) ring: the data of stage k0 + kd into the
         // buffer of stage ks (they differ only past the last stage, where a free buffer
         // takes a repeat of the last stage so that every phase issues the same loads)
         auto load_w = [&](int kd, int ks, int i) __attribute__((always_inline)) {
             uint8_t* dst = wring + (ks % NSW) * WSTAGE + wave * LPW_W * 1024;
-            const int chunk = lc ^ ((4 * i + (lane >> 4)) & 7);
+            const int chunk = lc ^ ((4 * LPW_W * wave + 4 * i + (lane >> 4)) & 7);
             const int k = (k0 + kd) * BK + 8 * chunk;
             const uint8_t* row = p.w + (size_t)min(w_v0 + 8 * i, vlast) * rowbytes;
             const uint8_t* src = (HFULL || k < H) ? row + (size_t)k * 2 : row;
@@ -407,7 +427,7 @@ __global__ __launch_bounds__(NT, 1) void head_tile_kernel(LmHeadArgs p) {
         };
         auto load_x = [&](int kd, int ks, int i) __attribute__((always_inline)) {
             uint8_t* dst = xring + (ks % NSX) * XSTAGE + wave * LPW_X * 1024;
-            const int chunk = lc ^ ((4 * i + 4 * wave + (lane >> 4)) & 7);
+            const int chunk = lc ^ ((4 * LPW_X * wave + 4 * i + (lane >> 4)) & 7);
             const int k = (k0 + kd) * BK + 8 * chunk;
             const int m = min(x_m0 + 8 * i, plast);
             const uint8_t* row = m < p.Mt ? p.xt + (size_t)m * rowbytes : p.xd + (size_t)(m - p.Mt) * rowbytes;
@@ -487,7 +507,7 @@ __global__ __launch_bounds__(NT, 1) void head_tile_kernel(LmHeadArgs p) {
             static_for<0, NR>([&](auto i) __attribute__((always_inline)) { rd(0, 0, a0, b0, i); });
             wait_lgkm0();
             for (int kb = 0; kb < nki; ++kb) {
-                mma_step<NL, NR>(acc, a0, b0, [&](auto i) __attribute__((always_inline)) { rd(kb, 1, a1, b1, i); });
+                mma_step<G, NL, NR>(acc, a0, b0, [&](auto i) __attribute__((always_inline)) { rd(kb, 1, a1, b1, i); });
                 wait_lgkm0();
                 if (kb + 1 < nki) {
                     // this wave's loads of stage kb + 1 are done when only later ones remain:
@@ -505,7 +525,7 @@ __global__ __launch_bounds__(NT, 1) void head_tile_kernel(LmHeadArgs p) {
                 // stage into buffers no longer read), so the wait counts above hold; after the
                 // last stage the reads below fetch stale LDS, never used.
                 const int kx = min(kb + NSX, nki - 1), kw = min(kb + NSW, nki - 1);
-                mma_step<NL, LPW_X + LPW_W + NR>(acc, a1, b1, [&](auto i_tag) __attribute__((always_inline)) {
+                mma_step<G, NL, LPW_X + LPW_W + NR>(acc, a1, b1, [&](auto i_tag) __attribute__((always_inline)) {
                     constexpr int i = decltype(i_tag)::value;
                     if constexpr (i < LPW_X) {
                         load_x(kx, kb + NSX, i);
@@ -523,7 +543,7 @@ __global__ __launch_bounds__(NT, 1) void head_tile_kernel(LmHeadArgs p) {
             asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
             if (piece >= 0) {
                 // a K piece: this wave's live accumulators out
-                f32x4_t* dst = reinterpret_cast<f32x4_t*>(p.tail) + (size_t)piece * piece_float4(p.tail_fm) + tid;
+                f32x4_t* dst = reinterpret_cast<f32x4_t*>(p.tail) + (size_t)piece * piece_float4<G>(p.tail_fm) + tid;
                 const int fl = p.tail_fm;
 #pragma unroll
                 for (int fv = 0; fv < FV; ++fv)
@@ -533,7 +553,7 @@ __global__ __launch_bounds__(NT, 1) void head_tile_kernel(LmHeadArgs p) {
         };
         with_live<FM>(t.nlive, stage_loop);
 
-        if (piece < 0) epilogue(p, t, acc, stats, tid, vh, mh);
+        if (piece < 0) epilogue<G>(p, t, acc, stats, tid, vh, mh);
         else stage_barrier();  // every wave is past its stage loop
     };
 
@@ -553,7 +573,9 @@ __global__ __launch_bounds__(NT, 1) void head_tile_kernel(LmHeadArgs p) {
 // takes tile tail_f + u. Each thread adds, in piece order, the raw accumulators that the
 // head kernel's thread (vh + 2 mh) * 64 + lane held for that fragment, runs frag_stats on
 // the sums and the halves are merged as in the head kernel's epilogue.
+template <class G>
 __global__ __launch_bounds__(128) void head_tile_tail_kernel(LmHeadArgs p) {
+    constexpr int FV = G::FV, FM = G::FM;
     __shared__ WStat stats[2][16];
     const int u = blockIdx.x / (2 * FM);
     const int mh = (blockIdx.x / FM) % 2;
@@ -574,7 +596,7 @@ __global__ __launch_bounds__(128) void head_tile_tail_kernel(LmHeadArgs p) {
         for (int kq = 0; kq < 4; ++kq) {
             if (k0 + kq < p.tail_ks) {
                 const f32x4_t* src = reinterpret_cast<const f32x4_t*>(p.tail) +
-                                     (size_t)(u + (k0 + kq) * p.tail_r) * piece_float4(fl) + fm * NT + tid;
+                                     (size_t)(u + (k0 + kq) * p.tail_r) * piece_float4<G>(fl) + fm * NT + tid;
 #pragma unroll
                 for (int fv = 0; fv < FV; ++fv) v[kq][fv] = src[(size_t)fv * fl * NT];
             }
@@ -586,7 +608,7 @@ __global__ __launch_bounds__(128) void head_tile_tail_kernel(LmHeadArgs p) {
                 for (int fv = 0; fv < FV; ++fv) a[fv] += v[kq][fv];
             }
     }
-    const WStat w = frag_stats(p, t, a, fm, lane & 15, lane >> 4);
+    const WStat w = frag_stats<G>(p, t, a, fm, lane & 15, lane >> 4);
     if ((lane >> 4) == 0) stats[vh][lane & 15] = w;
     __syncthreads();
     if (threadIdx.x < 16) {
@@ -600,7 +622,7 @@ __global__ __launch_bounds__(128) void head_tile_tail_kernel(LmHeadArgs p) {
 }
 
 // Raises the kernel's dynamic-LDS limit, once per device.
-template <bool NTW, bool PF, bool HFULL>
+template <class G, bool NTW, bool PF, bool HFULL>
 hipError_t allow_lds() {
     static std::atomic<uint64_t> done{0};  // bit d: done on device d (devices past 63: every call)
     int dev = 0;
@@ -608,46 +630,58 @@ hipError_t allow_lds() {
     if (e != hipSuccess) return e;
     const uint64_t bit = dev >= 0 && dev < 64 ? (1ull << dev) : 0ull;
     if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
-    e = hipFuncSetAttribute((const void*)head_tile_kernel<NTW, PF, HFULL>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            LDS);
+    e = hipFuncSetAttribute((const void*)head_tile_kernel<G, NTW, PF, HFULL>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            G::LDS);
     if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_release);
     return e;
 }
 
-template <bool NTW, bool PF, bool HFULL>
+template <class G, bool NTW, bool PF, bool HFULL>
 hipError_t launch_t(const Plan& plan, const LmHeadArgs& args, hipStream_t stream) {
-    const hipError_t e = allow_lds<NTW, PF, HFULL>();
+    const hipError_t e = allow_lds<G, NTW, PF, HFULL>();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((head_tile_kernel<NTW, PF, HFULL>), dim3(plan.grid), dim3(NT), LDS, stream, args);
+    hipLaunchKernelGGL((head_tile_kernel<G, NTW, PF, HFULL>), dim3(plan.grid), dim3(NT), G::LDS, stream, args);
     if (args.tail_r > 0) {
         const hipError_t le = hipGetLastError();
         if (le != hipSuccess) return le;
-        hipLaunchKernelGGL(head_tile_tail_kernel, dim3(args.tail_r * 2 * FM), dim3(128), 0, stream, args);
+        hipLaunchKernelGGL(head_tile_tail_kernel<G>, dim3(args.tail_r * 2 * G::FM), dim3(128), 0, stream, args);
     }
     return hipGetLastError();
 }
 
 template <bool HFULL>
 hipError_t launch_h(const Plan& plan, const LmHeadArgs& args, hipStream_t stream) {
-    // one chunk per tile: W streams once (non-temporal); several: shared, prefetched
-    return plan.MC == 1 ? launch_t<true, false, HFULL>(plan, args, stream)
-                        : launch_t<false, true, HFULL>(plan, args, stream);
+    // one chunk per tile: W streams once (non-temporal); several: shared, prefetched.
+    // The small geometry serves one chunk only.
+    if (plan.geo == 1) return launch_t<GeoS, true, false, HFULL>(plan, args, stream);
+    return plan.MC == 1 ? launch_t<GeoL, true, false, HFULL>(plan, args, stream)
+                        : launch_t<GeoL, false, true, HFULL>(plan, args, stream);
+}
+
+template <class G>
+bool geometry_fits(const Plan& plan, const LmHeadArgs& args) {
+    const int G16 = (plan.V + 15) / 16, Mf = (plan.Meff + 15) / 16;
+    // every tile at most 2 FV fragments, every chunk at most 2 FM
+    return (long long)plan.S * 2 * G::FV >= G16 && (long long)plan.MC * 2 * G::FM >= Mf &&
+           (args.tail_r == 0 || (args.tail_fm >= 1 && args.tail_fm <= G::FM));
 }
 
 }  // namespace
 
-size_t head_tile_lds_bytes() { return LDS; }
+int head_tile_max_positions(int geo) { return geo == 1 ? GeoS::BM : GeoL::BM; }
 
-int head_tile_max_positions() { return BM; }
+int head_tile_rows(int geo) { return geo == 1 ? GeoS::BV : GeoL::BV; }
 
-size_t head_tile_piece_bytes(int fm) { return (size_t)FV * fm * NT * 16; }
+size_t head_tile_piece_bytes(int fm, int geo) { return (size_t)(geo == 1 ? GeoS::FV : GeoL::FV) * fm * NT * 16; }
 
 hipError_t launch_head_tile(const Plan& plan, const LmHeadArgs& args, hipStream_t stream) {
     if (plan.grid % 8 != 0 || plan.grid < 8) return hipErrorInvalidConfiguration;
     // split tiles: one chunk, every piece a workgroup of the grid, a non-empty K range each
     if (args.tail_r > 0 && (plan.MC != 1 || args.tail == nullptr || args.tail_ks < 2 ||
                             args.tail_r * args.tail_ks > plan.grid || args.tail_f + args.tail_r != plan.S ||
-                            args.tail_ks > (plan.H + BK - 1) / BK || args.tail_fm < 1 || args.tail_fm > FM))
+                            args.tail_ks > (plan.H + BK - 1) / BK))
+        return hipErrorInvalidConfiguration;
+    if (plan.geo == 1 ? (plan.MC != 1 || !geometry_fits<GeoS>(plan, args)) : !geometry_fits<GeoL>(plan, args))
         return hipErrorInvalidConfiguration;
     return plan.H % BK == 0 ? launch_h<true>(plan, args, stream) : launch_h<false>(plan, args, stream);
 }

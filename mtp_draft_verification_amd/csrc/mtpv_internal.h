@@ -61,6 +61,7 @@ struct Plan {
     int tail_f, tail_r, tail_ks;  // tiled kernel, one position chunk: tiles [tail_f, tail_f + tail_r) are
                                   // split along K in tail_ks pieces (0 tail tiles: none split)
     int tail_fm;                  // live position fragments per wave of those tiles
+    int geo;                      // tiled kernel: 0 = 256-row x 224-position tiles, 1 = 192 x 128
     int NJ;          // inverse-CDF jobs (0 in greedy mode)
     int C;           // chunks per job in the residual passes
     int ntiles;      // 64-element tiles per vocabulary row
@@ -102,8 +103,9 @@ hipError_t launch_lmhead(const Plan& plan, const LmHeadArgs& args, hipStream_t s
 hipError_t launch_skinny(const Plan& plan, const LmHeadArgs& args, hipStream_t stream);
 hipError_t launch_wide(const Plan& plan, const LmHeadArgs& args, hipStream_t stream);
 hipError_t launch_head_tile(const Plan& plan, const LmHeadArgs& args, hipStream_t stream);
-int head_tile_max_positions();  // positions per chunk of the persistent tiled kernel
-size_t head_tile_piece_bytes(int fm);  // raw accumulators of one K piece of a split tile (fm live fragments)
+int head_tile_max_positions(int geo);  // positions per chunk of the persistent tiled kernel's geometry
+int head_tile_rows(int geo);           // vocabulary rows per tile of that geometry
+size_t head_tile_piece_bytes(int fm, int geo);  // raw accumulators of one K piece of a split tile (fm live fragments)
 size_t wide_lds_bytes(int bm);  // dynamic LDS of the wide kernel for bm (64, 128 or 256) positions per tile
 int wide_rows();                // most vocabulary rows per wide-kernel tile
 

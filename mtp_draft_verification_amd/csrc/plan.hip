@@ -102,20 +102,25 @@ int make_plan(int mode, int B, int k, int H, int V, int dtype, Plan* pl, int man
     if (many_kind == KIND_HTILE && !wide_forced() && p.kind != KIND_SKINNY && p.es == 2 &&
         p.Meff > kWideMaxRows) {
         // Many positions, bf16: the persistent tiled kernel. Position chunks of at most
-        // 14 fragments (224 positions), split evenly; vocabulary tiles of at most 16
-        // fragments (256 rows), as many as make whole rounds of items over the compute
-        // units (tile edges on 16-row boundaries, every tile at least one fragment).
+        // the geometry's positions, split evenly; vocabulary tiles of at most its rows, as
+        // many as make whole rounds of items over the compute units (tile edges on 16-row
+        // boundaries, every tile at least one fragment).
         p.kind = KIND_HTILE;
-        const int cap = head_tile_max_positions() / 16;
+        // At most 128 head rows (one chunk of the small geometry): 192-row tiles with five
+        // W stages, four of them in flight, since there the W stream sets the pace; more
+        // rows: 256-row x 224-position tiles with three W stages.
         const long long Mf = (p.Meff + 15) / 16;
+        p.geo = Mf <= head_tile_max_positions(1) / 16 ? 1 : 0;
+        const int cap = head_tile_max_positions(p.geo) / 16;
+        const int tfr = head_tile_rows(p.geo) / 16;  // fragments per whole tile
         p.MC = (int)((Mf + cap - 1) / cap);
         const long long G = (V + 15) / 16;
-        const long long nvt_min = (G + 15) / 16;
+        const long long nvt_min = (G + tfr - 1) / tfr;
         const long long rounds = (nvt_min * p.MC + kCUs - 1) / kCUs;
         long long S = std::max(nvt_min, rounds * kCUs / p.MC);
         S = std::min(S, G);
-        // One position chunk and whole 256-row tiles that leave the last round part
-        // full: the whole rounds as they are, the tiles left over cut along K into
+        // One position chunk and whole tiles that leave the last round part full: the
+        // whole rounds as they are, the tiles left over cut along K into
         // pieces that fill the compute units instead (raw accumulators to the
         // workspace, added in piece order by a second kernel that finishes those
         // tiles). Padding the rounds with smaller tiles instead keeps the MFMA work of
@@ -132,7 +137,7 @@ int make_plan(int mode, int B, int k, int H, int V, int dtype, Plan* pl, int man
         p.S = (int)S;
         const long long items = S * p.MC;
         p.grid = (int)std::min<long long>(kCUs, (items + 7) / 8 * 8);
-        p.nt = head_tile_max_positions();
+        p.nt = head_tile_max_positions(p.geo);
         p.kc = 64;
         p.lds = 0;
         p.vblock = 0;
@@ -213,7 +218,7 @@ int make_plan(int mode, int B, int k, int H, int V, int dtype, Plan* pl, int man
     p.off_spill = off;
     if (mode != MTPV_MODE_GREEDY) off = align_up(off + (size_t)p.Meff * V * sizeof(float), 256);
     p.off_tail = off;
-    off = align_up(off + (size_t)p.tail_r * p.tail_ks * head_tile_piece_bytes(p.tail_fm), 256);
+    off = align_up(off + (size_t)p.tail_r * p.tail_ks * head_tile_piece_bytes(p.tail_fm, p.geo), 256);
     p.total = off;
     *pl = p;
     return MTPV_OK;
