@@ -1,4 +1,4 @@
-// LM-head kernel for many positions (more than 16, bf16): batched verification,
+// LM-head kernel for many positions (more than 96, bf16): batched verification,
 // the depth-5 chain and the large-batch rollout shape.
 //
 // The verify pass is a contraction l[m, v] = sum_h x[m, h] W[v, h] over every target
@@ -14,22 +14,27 @@
 //    a tile next to each other: the workgroups of one XCD work on the chunks of the
 //    same tiles at the same time, so each W tile comes from HBM once and from that
 //    XCD's L2 for the other chunks;
-//  * a tile is at most 256 vocabulary rows (16 fragments of 16 rows) by at most 224
-//    positions (14 fragments), each split in two halves: wave w owns vocabulary half
-//    w % 2 (up to 128 rows) and position half w / 2 (up to 112 positions), 8 x 7
-//    accumulators of 16x16x32 bf16 MFMAs, one wave per SIMD. Per K-step a wave reads
-//    15 fragments from LDS for 56 MFMAs (a 64 x 128 wave tile would read 12 for 32);
+//  * a tile is at most 2 FV x 16 vocabulary rows by 2 FM x 16 positions, each split
+//    in two halves: wave w owns vocabulary half w % 2 and position half w / 2, FV x FM
+//    accumulators of 16x16x32 bf16 MFMAs in AGPRs, one wave per SIMD. Two geometries:
+//    FV x FM = 8 x 7 (256 x 224 tiles; per K-step a wave reads 15 fragments from LDS
+//    for 56 MFMAs) and, for at most 128 positions, 6 x 4 (192 x 128) with a deeper W
+//    ring;
 //  * both operands are staged in LDS in K-stages of 64 hidden elements (128 bytes per
 //    row) with 16-byte direct-to-LDS loads (one instruction = 8 whole 128-byte rows),
-//    3 stages of W and 2 of positions; 16-byte chunks XOR-swizzled by row so the
-//    fragment reads have no bank conflicts;
+//    3 (or 5) stages of W and 2 of positions; 16-byte chunks XOR-swizzled by row so
+//    the fragment reads have no bank conflicts;
 //  * a wave whose position half ends early skips the padded fragments' reads and
 //    MFMAs (one instance of the stage loop per live-fragment count);
 //  * after the last stage each wave folds its logits into per-position statistics
 //    (max of l * c2, sum of exp2, argmax), gathers the draft logits and writes the fp32
 //    logits out when asked; the two vocabulary halves are merged in LDS into one
-//    partial per (position, vocabulary tile).
-// Accumulation is fp32 over all of H in a fixed order, no atomics.
+//    partial per (position, vocabulary tile);
+//  * with one position chunk, the vocabulary tiles left over after whole rounds are
+//    cut along K into pieces run by otherwise idle workgroups; head_tile_tail_kernel
+//    adds the pieces' raw accumulators and runs the same epilogue.
+// Accumulation is fp32 over all of H in a fixed order (split tiles: the pieces in
+// order), no atomics.
 #include "mtpv_internal.h"
 
 #include <algorithm>
