@@ -214,8 +214,9 @@ int run(const Plan& plan, const void* xt, const void* xd, const void* w, const i
         ra.NJ = plan.NJ;
         ra.V = plan.V;
         ra.C = plan.C;
+        ra.tpc = plan.tpc;
         ra.ntiles = plan.ntiles;
-        ra.inv_t = 1.0 / T;
+        ra.c2d = 1.442695040888963407359924681001892137 / T;
         ra.zpart = zpart;
         ra.tsum = tsum;
         ra.out = plan.mode == MTPV_MODE_DRAFT ? const_cast<int32_t*>(drafts) : out;

@@ -35,7 +35,7 @@ struct Job {
     int out_index;  // element of the output token array to write
     int pad;
     double u;       // uniform in [0, 1)
-    double ref_p;   // reference (about the row max of l / T) for the fp64 exponentials
+    double ref_p;   // reference: the row max of l log2(e) / T (log2 units) for the exponentials
     double ref_q;
 };
 
@@ -64,6 +64,7 @@ struct Plan {
     int geo;                      // tiled kernel: 0 = 256-row x 224-position tiles, 1 = 192 x 128
     int NJ;          // inverse-CDF jobs (0 in greedy mode)
     int C;           // chunks per job in the residual passes
+    int tpc;         // tiles per chunk (a multiple of the passes' 64-tile trip)
     int ntiles;      // 64-element tiles per vocabulary row
     // workspace layout (byte offsets)
     size_t off_err, off_partials, off_dlogit, off_rowstat, off_jobs, off_zpart, off_tsum, off_spill, off_tail;
@@ -133,8 +134,8 @@ hipError_t launch_decide(const Plan& plan, const DecideArgs& args, hipStream_t s
 struct ResidualArgs {
     const float* logits;    // spilled logits [Meff, V]
     const Job* jobs;
-    int NJ, V, C, ntiles;
-    double inv_t;
+    int NJ, V, C, tpc, ntiles;
+    double c2d;             // log2(e) / T in fp64
     double* zpart;          // [NJ, C, 2]
     double* tsum;           // [NJ, ntiles]
     int32_t* out;           // token output array (indexed by Job::out_index)

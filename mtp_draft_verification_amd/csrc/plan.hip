@@ -195,9 +195,19 @@ int make_plan(int mode, int B, int k, int H, int V, int dtype, Plan* pl, int man
     p.ntiles = (V + 63) / 64;
     p.NJ = mode == MTPV_MODE_GREEDY ? 0 : mode == MTPV_MODE_SAMPLE ? B : B * k;
     if (p.NJ > 0) {
+        // About 1024 workgroups over all jobs where V allows, each chunk a whole number
+        // of the passes' 64-tile trips (no half-empty trips), at most 64 chunks per job.
+        // Short chunks are rounded down (more workgroups hide more latency); long ones
+        // are rounded up when rounding down would pass the 1024 workgroups resident at
+        // once (4 per compute unit), which would leave a second round of long chunks.
         int c = (1024 + p.NJ - 1) / p.NJ;
         c = std::max(1, std::min(c, 64));
-        p.C = std::min(c, p.ntiles);
+        const int trip = 64;
+        p.tpc = std::max(trip, p.ntiles / c / trip * trip);
+        const long long wgs = (long long)p.NJ * ((p.ntiles + p.tpc - 1) / p.tpc);
+        if ((p.ntiles + p.tpc - 1) / p.tpc > 64 || (wgs > 1024 && p.tpc >= 4 * trip))
+            p.tpc = ((p.ntiles + c - 1) / c + trip - 1) / trip * trip;
+        p.C = (p.ntiles + p.tpc - 1) / p.tpc;
     }
     // workspace layout
     size_t off = 0;

@@ -21,6 +21,7 @@
 // consistent and bit-reproducible.
 #include "mtpv_internal.h"
 
+#include <algorithm>
 #include <climits>
 
 namespace mtpv {
@@ -81,14 +82,17 @@ __device__ __forceinline__ int request_row(const DecideArgs& p, int b, int i) {
     return p.Mt + b * p.k + (i - p.k - 1);
 }
 
-// One workgroup per request. Wave w merges rows w, w + 4, ... of the request:
+// One workgroup per request, one wave per row up to 8 waves. Wave w of nw merges
+// rows w, w + nw, ... of the request:
 // each lane loads its share of the row's S partials (all loads of a batch issued
 // before any use), reduces them (max first, then one exp2 per partial, no serial
 // exp chain), and a wave butterfly finishes the row; all in a fixed order. While
 // the waves reduce, the decision inputs (draft ids, draft logits, Philox uniforms)
 // are fetched by other lanes. Then one slot per thread is decided and thread 0
 // scans for the first rejection. Draft mode only writes one sampling job per row.
-__global__ __launch_bounds__(256) void decide_kernel(DecideArgs p) {
+constexpr int kDecideWaves = 8;
+
+__global__ __launch_bounds__(64 * kDecideWaves) void decide_kernel(DecideArgs p) {
     constexpr int U = 16;
     __shared__ RowStat rows[129];
     __shared__ int s_draft[64];
@@ -98,6 +102,7 @@ __global__ __launch_bounds__(256) void decide_kernel(DecideArgs p) {
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
+    const int nw = blockDim.x >> 6;
     const int k = p.k;
     const int nrows = p.mode == 0 ? k + 1 : p.mode == 1 ? 2 * k + 1 : k;
     // drafts judged for this request (k_b <= k; the rest of its rows are unused)
@@ -110,10 +115,10 @@ __global__ __launch_bounds__(256) void decide_kernel(DecideArgs p) {
     const float ninf = -__builtin_inff();
 
     // Decision inputs, independent of the row statistics. They are fetched by the
-    // last wave (after its rows' loads are issued) so no wave's partial loads wait
-    // behind them; the draft-logit loads do not depend on the draft ids (a logit
-    // slot of an out-of-range draft is never written and never used).
-    const int fetch_wave = min(3, max(0, nrows - 1) % 4);
+    // wave of the last row (after its row's loads are issued) so no wave's partial
+    // loads wait behind them; the draft-logit loads do not depend on the draft ids (a
+    // logit slot of an out-of-range draft is never written and never used).
+    const int fetch_wave = max(0, nrows - 1) % nw;
     auto fetch_inputs = [&]() {
         if (p.mode != 2 && wave == fetch_wave && lane < k) {
             const int j = lane;
@@ -128,7 +133,7 @@ __global__ __launch_bounds__(256) void decide_kernel(DecideArgs p) {
     };
     if (wave >= nrows) fetch_inputs();
 
-    for (int i = wave; i < nrows; i += 4) {
+    for (int i = wave; i < nrows; i += nw) {
         const int r = request_row(p, b, i);
         const Partial* row = p.partials + (size_t)r * p.S;
         // Pass 1 over the row (usually one batch held in registers): the row max.
@@ -146,7 +151,7 @@ __global__ __launch_bounds__(256) void decide_kernel(DecideArgs p) {
                 const int s = base + u * 64 + lane;
                 q[u] = s < p.S ? row[s] : Partial{ninf, 0.f, ninf, INT_MAX};
             }
-            if (base == 0 && i + 4 >= nrows) fetch_inputs();  // overlap with this wave's loads
+            if (base == 0 && i + nw >= nrows) fetch_inputs();  // overlap with this wave's loads
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 m = fmaxf(m, q[u].x);
@@ -204,7 +209,7 @@ __global__ __launch_bounds__(256) void decide_kernel(DecideArgs p) {
                 job.out_index = r;
                 job.pad = 0;
                 job.u = slot_uniform(p.seed, p.offset, p.depth0 + i, b, 2);
-                job.ref_p = a.x * kLn2;
+                job.ref_p = a.x;
                 job.ref_q = 0.0;
                 p.jobs[r] = job;
             }
@@ -261,8 +266,8 @@ __global__ __launch_bounds__(256) void decide_kernel(DecideArgs p) {
         job.out_index = b * (k + 1) + al;
         job.pad = 0;
         job.u = slot_uniform(p.seed, p.offset, al, b, 1);
-        job.ref_p = rows[al].x * kLn2;
-        job.ref_q = (al < kb) ? rows[k + 1 + al].x * kLn2 : 0.0;
+        job.ref_p = rows[al].x;
+        job.ref_q = (al < kb) ? rows[k + 1 + al].x : 0.0;
         p.jobs[b] = job;
     }
 }
@@ -303,25 +308,30 @@ __device__ __forceinline__ F4 row_logit4(const float* logits, int row, int V, in
     return r;
 }
 
-// exp(l / T - ref) as 2^n * 2^f: t = (l / T - ref) log2(e) in fp64, n = round(t),
-// f = t - n in [-1/2, 1/2], 2^f from the hardware fp32 exp2 of f (f exact to 2^-25,
-// the result to about 1e-7 relative), scaled by 2^n exactly. The error is a small
-// random relative factor per element: the job's normaliser sums these same values,
-// so a common scale cancels, and the cumulative sums stay in fp64.
-__device__ __forceinline__ double row_exp_of(float l, bool live, double inv_t, double ref) {
+// exp(l / T) up to the job's common factor, as 2^n * 2^f: t = l log2(e) / T - ref in
+// fp64 (ref: the row max in log2 units), n = round(t), f = t - n in [-1/2, 1/2], 2^f
+// from the hardware exp2 (f exact to 2^-25, no range reduction needed in that
+// interval, the result to about 1e-7 relative), scaled by 2^n exactly. The error is a
+// small random relative factor per element: the job's normaliser sums these same
+// values, so a common scale cancels, and the cumulative sums stay in fp64.
+__device__ __forceinline__ double row_exp_of(float l, bool live, double c2d, double ref) {
     if (!live) return 0.0;
-    const double t = fma((double)l, inv_t, -ref) * 1.442695040888963407359924681001892137;
+    const double t = fma((double)l, c2d, -ref);
     const double n = rint(t);
-    return ldexp((double)exp2f((float)(t - n)), (int)n);
+    return ldexp((double)__builtin_amdgcn_exp2f((float)(t - n)), (int)n);
 }
+
+// Holds a wave-uniform job constant in a vector register once, so the fma above (which
+// may read only one scalar operand on this chip) does not copy it in per element.
+__device__ __forceinline__ void in_vgpr(double& x) { asm volatile("" : "+v"(x)); }
 
 // Weight of one element for a job from its two logits: max(0, p - q) with a drafter
 // row, else p; rp and rq are the reciprocals of the rows' normalisers.
-__device__ __forceinline__ double weight_of(float lp, float lq, bool live, bool use_q, double inv_t, const Job& job,
+__device__ __forceinline__ double weight_of(float lp, float lq, bool live, bool use_q, double c2d, const Job& job,
                                             double rp, double rq) {
-    const double pv = row_exp_of(lp, live, inv_t, job.ref_p) * rp;
+    const double pv = row_exp_of(lp, live, c2d, job.ref_p) * rp;
     if (!use_q) return pv;
-    const double qv = row_exp_of(lq, live, inv_t, job.ref_q) * rq;
+    const double qv = row_exp_of(lq, live, c2d, job.ref_q) * rq;
     const double d = pv - qv;
     return d > 0.0 ? d : 0.0;
 }
@@ -335,11 +345,11 @@ struct Lane4 {
     double s;  // ((w0 + w1) + w2) + w3
 };
 
-__device__ __forceinline__ Lane4 lane_weights(const F4& lp, const F4& lq, int v, int vend, bool use_q, double inv_t,
+__device__ __forceinline__ Lane4 lane_weights(const F4& lp, const F4& lq, int v, int vend, bool use_q, double c2d,
                                               const Job& job, double rp, double rq) {
     Lane4 r;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) r.w[e] = weight_of(lp.a[e], lq.a[e], v + e < vend, use_q, inv_t, job, rp, rq);
+    for (int e = 0; e < 4; ++e) r.w[e] = weight_of(lp.a[e], lq.a[e], v + e < vend, use_q, c2d, job, rp, rq);
     r.s = ((r.w[0] + r.w[1]) + r.w[2]) + r.w[3];
     return r;
 }
@@ -362,14 +372,19 @@ __device__ __forceinline__ double wave_scan(double x, int lane) {
     return x;
 }
 
-// Reciprocals of the job's normalisers (sums of the fixed-order chunk partials).
+// Reciprocals of the job's normalisers: lane c of each wave loads chunk c's partials
+// (C <= 64) and a butterfly adds them; every lane ends with the same sums, in the
+// same order wherever this is called.
 __device__ __forceinline__ void normalisers(const ResidualArgs& p, int j, double* rp, double* rq) {
-    double a = 0.0, b = 0.0;
+    const int lane = threadIdx.x & 63;
     const double* zpart = p.zpart + (size_t)j * p.C * 2;
-    for (int c = 0; c < p.C; ++c) {
-        a += zpart[2 * c];
-        b += zpart[2 * c + 1];
+    double a = 0.0, b = 0.0;
+    if (lane < p.C) {
+        a = zpart[2 * lane];
+        b = zpart[2 * lane + 1];
     }
+    a = wave_sum(a);
+    b = wave_sum(b);
     *rp = 1.0 / a;
     *rq = 1.0 / b;
 }
@@ -384,11 +399,12 @@ template <bool VEC>
 __global__ __launch_bounds__(256) void zsum_kernel(ResidualArgs p) {
     __shared__ double sh[2][4];
     const int j = blockIdx.y, c = blockIdx.x;
-    const Job job = p.jobs[j];
+    Job job = p.jobs[j];
+    in_vgpr(job.ref_p);
+    in_vgpr(job.ref_q);
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int tpc = (p.ntiles + p.C - 1) / p.C;
-    const int t0 = c * tpc, t1 = min(p.ntiles, t0 + tpc);
+    const int t0 = c * p.tpc, t1 = min(p.ntiles, t0 + p.tpc);
     const int e1 = min(p.V, t1 * 64);
     const bool has_q = job.row_q >= 0;
     double sp = 0.0, sq = 0.0;
@@ -409,15 +425,15 @@ __global__ __launch_bounds__(256) void zsum_kernel(ResidualArgs p) {
             lp[i] = np[i];
             lq[i] = nq[i];
         }
-        fetch(base + 1024 * UR);
+        if (base + 1024 * UR < e1) fetch(base + 1024 * UR);
 #pragma unroll
         for (int i = 0; i < UR; ++i) {
             const int v = base + 1024 * i + 4 * tid;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const bool live = v + e < e1;
-                sp += row_exp_of(lp[i].a[e], live, p.inv_t, job.ref_p);
-                sq += row_exp_of(lq[i].a[e], live && has_q, p.inv_t, job.ref_q);
+                sp += row_exp_of(lp[i].a[e], live, p.c2d, job.ref_p);
+                sq += row_exp_of(lq[i].a[e], live && has_q, p.c2d, job.ref_q);
             }
         }
     }
@@ -441,14 +457,13 @@ __global__ __launch_bounds__(256) void zsum_kernel(ResidualArgs p) {
 template <bool VEC>
 __global__ __launch_bounds__(256) void tsum_kernel(ResidualArgs p) {
     const int j = blockIdx.y, c = blockIdx.x;
-    const Job job = p.jobs[j];
+    Job job = p.jobs[j];
+    in_vgpr(job.ref_p);
+    in_vgpr(job.ref_q);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, q = lane & 15;
-    double rp, rq;
-    normalisers(p, j, &rp, &rq);
     const bool use_q = job.row_q >= 0;
-    const int tpc = (p.ntiles + p.C - 1) / p.C;
-    const int t0 = c * tpc, t1 = min(p.ntiles, t0 + tpc);
+    const int t0 = c * p.tpc, t1 = min(p.ntiles, t0 + p.tpc);
     F4 np[UR], nq[UR];
     auto fetch = [&](int tb) {
 #pragma unroll
@@ -459,6 +474,8 @@ __global__ __launch_bounds__(256) void tsum_kernel(ResidualArgs p) {
         }
     };
     fetch(t0 + 4 * wave + g);
+    double rp, rq;  // (their loads wait behind the first logits)
+    normalisers(p, j, &rp, &rq);
     for (int tb = t0 + 4 * wave + g; tb < t1; tb += 16 * UR) {  // uniform within each 16-lane group
         F4 lp[UR], lq[UR];
 #pragma unroll
@@ -466,15 +483,23 @@ __global__ __launch_bounds__(256) void tsum_kernel(ResidualArgs p) {
             lp[i] = np[i];
             lq[i] = nq[i];
         }
-        fetch(tb + 16 * UR);
+        if (tb + 16 * UR < t1) fetch(tb + 16 * UR);
 #pragma unroll
         for (int i = 0; i < UR; ++i) {
             const int t = tb + 16 * i;
-            const Lane4 w = lane_weights(lp[i], lq[i], t * 64 + 4 * q, p.V, use_q, p.inv_t, job, rp, rq);
+            const Lane4 w = lane_weights(lp[i], lq[i], t * 64 + 4 * q, p.V, use_q, p.c2d, job, rp, rq);
             const double incl = scan16(w.s, q);
             if (q == 15 && t < t1) p.tsum[(size_t)j * p.ntiles + t] = incl;
         }
     }
+}
+
+// Tile sums [i, i + SB) of a thread's run (0.0 past its end i1), all loads issued
+// before any is used.
+constexpr int SB = 16;
+__device__ __forceinline__ void load_sums(const double* ts, int i, int i1, double (&tb)[SB]) {
+#pragma unroll
+    for (int u = 0; u < SB; ++u) tb[u] = i + u < i1 ? ts[i + u] : 0.0;
 }
 
 // Pass 3: locate u * (total weight) in the fixed-order sums and emit the token.
@@ -487,7 +512,9 @@ __global__ __launch_bounds__(256) void search_kernel(ResidualArgs p) {
     const int j = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const Job job = p.jobs[j];
+    Job job = p.jobs[j];
+    in_vgpr(job.ref_p);
+    in_vgpr(job.ref_q);
     double rp, rq;
     normalisers(p, j, &rp, &rq);
     bool use_q = job.row_q >= 0;
@@ -502,7 +529,7 @@ __global__ __launch_bounds__(256) void search_kernel(ResidualArgs p) {
             for (int tb = 4 * wave + g; tb < p.ntiles; tb += 16) {  // uniform within each 16-lane group
                 const int v = tb * 64 + 4 * q;
                 const F4 lp = row_logit4<VEC>(p.logits, job.row_p, p.V, v);
-                const Lane4 w = lane_weights(lp, lp, v, p.V, false, p.inv_t, job, rp, rq);
+                const Lane4 w = lane_weights(lp, lp, v, p.V, false, p.c2d, job, rp, rq);
                 const double incl = scan16(w.s, q);
                 if (q == 15 && tb < p.ntiles) ts[tb] = incl;
             }
@@ -513,12 +540,16 @@ __global__ __launch_bounds__(256) void search_kernel(ResidualArgs p) {
         // walk its own tiles from there. The first tile (over all threads) whose running
         // sum passes the target is the draw's tile; its base is the running sum before it.
         const int i0 = min(p.ntiles, tid * per), i1 = min(p.ntiles, i0 + per);
-        double tot = 0.0;
+        double tot = 0.0;  // (adding the 0.0 of a padded slot leaves the sum as it is)
         int lastpos_tile = -1;
-        for (int i = i0; i < i1; ++i) {
-            const double t = ts[i];
-            tot += t;
-            if (t > 0.0) lastpos_tile = i;
+        for (int i = i0; i < i1; i += SB) {
+            double tb[SB];
+            load_sums(ts, i, i1, tb);
+#pragma unroll
+            for (int u = 0; u < SB; ++u) {
+                tot += tb[u];
+                if (tb[u] > 0.0) lastpos_tile = i + u;
+            }
         }
         const double incl = wave_scan(tot, lane);
         double excl = __shfl_up(incl, 1);
@@ -551,15 +582,18 @@ __global__ __launch_bounds__(256) void search_kernel(ResidualArgs p) {
             const double target = job.u * R;
             double run = wbase + excl;
             int cand = -1;
-            for (int i = i0; i < i1; ++i) {
-                const double t = ts[i];
-                if (run + t > target) {
-                    cand = i;
-                    atomicMin(&sh_tile, i);
-                    break;
+            for (int i = i0; i < i1 && cand < 0; i += SB) {
+                double tb[SB];
+                load_sums(ts, i, i1, tb);
+#pragma unroll
+                for (int u = 0; u < SB; ++u) {
+                    if (cand < 0 && i + u < i1) {
+                        if (run + tb[u] > target) cand = i + u;
+                        else run += tb[u];
+                    }
                 }
-                run += t;
             }
+            if (cand >= 0) atomicMin(&sh_tile, cand);
             if (lastpos_tile >= 0) atomicMax(&sh_last, lastpos_tile);
             __syncthreads();
             const int tile = sh_tile;
@@ -585,7 +619,7 @@ __global__ __launch_bounds__(256) void search_kernel(ResidualArgs p) {
             const int v = sh_pick * 64 + 4 * q;
             const F4 lp = row_logit4<VEC>(p.logits, job.row_p, p.V, v);
             const F4 lq = row_logit4<VEC>(p.logits, use_q ? job.row_q : job.row_p, p.V, v);
-            const Lane4 w = lane_weights(lp, lq, v, p.V, use_q, p.inv_t, job, rp, rq);
+            const Lane4 w = lane_weights(lp, lq, v, p.V, use_q, p.c2d, job, rp, rq);
             const double incl = scan16(w.s, q);
             double excl = __shfl_up(incl, 1, 16);
             if (q == 0) excl = 0.0;
@@ -634,7 +668,10 @@ __global__ __launch_bounds__(256) void copy_kernel(uint4* __restrict__ dst, cons
 }  // namespace
 
 hipError_t launch_decide(const Plan& plan, const DecideArgs& args, hipStream_t stream) {
-    hipLaunchKernelGGL(decide_kernel, dim3(plan.B), dim3(256), 0, stream, args);
+    const int nrows = args.mode == 0 ? args.k + 1 : args.mode == 1 ? 2 * args.k + 1 : args.k;
+    // one wave per row, up to 8 (the first wave alone covers the k <= 64 decision slots)
+    const int nw = std::max(1, std::min(kDecideWaves, nrows));
+    hipLaunchKernelGGL(decide_kernel, dim3(plan.B), dim3(64 * nw), 0, stream, args);
     return hipGetLastError();
 }
 
