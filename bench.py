@@ -223,6 +223,39 @@ def roofline_of(alg_bytes, alg_flops, kern_s, traffic_bytes=None):
     return r
 
 
+def achievable(W):
+    """What plain kernels reach on this machine beside the published peaks (measured after
+    the timed loop, outside it): one non-temporal read sweep of the head W's bytes,
+    and back-to-back bf16 MFMAs (16x16x32) on every SIMD; median of 5 launches each,
+    timed with events on the stream the library launches on."""
+    import torch
+    import mtp_draft_verification_amd as mv
+    sink = torch.zeros(4, dtype=torch.int32, device=W.device)
+    nbytes = W.numel() * W.element_size() // 16 * 16
+
+    def median_s(fn, reps=5):
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / 1e3)
+        return float(np.median(ts))
+
+    mv.read_bytes(W, nbytes, sink)
+    t_read = median_s(lambda: mv.read_bytes(W, nbytes, sink))
+    iters = 1024
+    flops = mv.mfma_rate(iters, sink)
+    t_mfma = median_s(lambda: mv.mfma_rate(iters, sink))
+    return {"hbm_read_gbs": round(nbytes / t_read / 1e9, 1), "read_bytes": int(nbytes),
+            "mfma_bf16_tflops": round(flops / t_mfma / 1e12, 1), "mfma_flops": int(flops),
+            "how": "mtpv_read_bytes over the head W (non-temporal 16-byte loads, contiguous ranges); "
+                   "mtpv_mfma_rate (4 waves per CU, 16 independent 16x16x32 bf16 MFMAs per round, varied "
+                   "operand bits); median of 5 launches"}
+
+
 def timing_every(steps):
     """Time one launch in this many during a rate loop of `steps` calls (at least
     about 32 timed launches; every launch for short loops)."""
@@ -529,6 +562,11 @@ def bench_verify(args, wl, mode):
     traffic = recorded_traffic(wl, mode)
     roofline = roofline_of(alg_bytes, alg_flops, kern_s, traffic)
     roofline["timed_launches"] = nlaunch
+    ach = achievable(Wd)
+    roofline["achievable"] = ach
+    roofline["frac_of_achievable"] = round(
+        roofline["mfma_tflops"] / ach["mfma_bf16_tflops"] if roofline["bound"] == "mfma"
+        else roofline["hbm_gbs"] / ach["hbm_read_gbs"], 4)
     line = {
         "metric": "verified positions/s (accepted tokens/s alongside) at 1 GPU; % of HBM roofline",
         "value": round(value, 1),

@@ -339,6 +339,26 @@ MTPV_API int mtpv_timing_read(double* ms_total, int64_t* launches, int reset);
  */
 MTPV_API int mtpv_copy_bytes(void* dst, const void* src, size_t bytes, void* stream);
 
+/*
+ * Achievable-rate probes, for reporting the verify kernels against what plain
+ * kernels reach on the same part (beside the published peaks). Measurement only:
+ * they compute nothing of the method and write nothing the caller reads.
+ *
+ * mtpv_read_bytes: one read sweep of `bytes` bytes at `src` (device pointer,
+ * 16-byte aligned, bytes % 16 == 0; 0 bytes launches nothing) with 16-byte
+ * non-temporal loads, each workgroup on its own contiguous range. `sink` is a
+ * 4-byte-aligned device word the kernel could write but never does. Errors:
+ * MTPV_ENULL, MTPV_EALIGN, MTPV_ELAUNCH.
+ *
+ * mtpv_mfma_rate: 256 workgroups of 4 waves, each wave issuing `iters` rounds of 16
+ * independent v_mfma_f32_16x16x32_bf16 (bf16 operands of magnitude 0.5 to 2 with
+ * varied bits, fp32 accumulation in registers); *flops receives the flops of the
+ * launch (256 * 4 * iters * 16 * 16384). `sink` as above. iters in [1, 2^24], else
+ * MTPV_EINVAL. Time either with events on `stream`.
+ */
+MTPV_API int mtpv_read_bytes(const void* src, size_t bytes, void* sink, void* stream);
+MTPV_API int mtpv_mfma_rate(int iters, void* sink, int64_t* flops, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

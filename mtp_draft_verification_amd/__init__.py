@@ -78,6 +78,8 @@ _SIGNATURES = {
     "mtpv_timing_enable": (_i, [_i]),
     "mtpv_timing_read": (_i, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), _i]),
     "mtpv_copy_bytes": (_i, [_vp, _vp, _sz, _vp]),
+    "mtpv_read_bytes": (_i, [_vp, _sz, _vp, _vp]),
+    "mtpv_mfma_rate": (_i, [_i, _vp, ctypes.POINTER(ctypes.c_int64), _vp]),
 }
 
 EXPORTED = tuple(_SIGNATURES)
@@ -334,3 +336,17 @@ def timing_read(reset=True):
 
 def copy_bytes(dst, src, nbytes, stream=None):
     _check(lib().mtpv_copy_bytes(_ptr(dst), _ptr(src), int(nbytes), _stream(stream)), "mtpv_copy_bytes")
+
+
+def read_bytes(src, nbytes, sink, stream=None):
+    """Achievable-rate probe: one non-temporal read sweep of nbytes at src (a device
+    tensor); sink: a device tensor of at least 4 bytes (never written)."""
+    _check(lib().mtpv_read_bytes(_ptr(src), int(nbytes), _ptr(sink), _stream(stream)), "mtpv_read_bytes")
+
+
+def mfma_rate(iters, sink, stream=None):
+    """Achievable-rate probe: back-to-back bf16 MFMAs on every SIMD; returns the flops
+    of the launch. sink: a device tensor of at least 4 bytes (never written)."""
+    flops = ctypes.c_int64(0)
+    _check(lib().mtpv_mfma_rate(int(iters), _ptr(sink), ctypes.byref(flops), _stream(stream)), "mtpv_mfma_rate")
+    return int(flops.value)

@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libmtpv.so")
 ARCH = os.environ.get("MTPV_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["api.hip", "plan.hip", "lmhead.hip", "skinny.hip", "wide.hip", "headtile.hip", "verify.hip", "fuse.hip",
-           "loss.hip"]
+           "loss.hip", "ceiling.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",

@@ -537,4 +537,22 @@ int mtpv_copy_bytes(void* dst, const void* src, size_t bytes, void* stream) {
     return MTPV_OK;
 }
 
+int mtpv_read_bytes(const void* src, size_t bytes, void* sink, void* stream) {
+    if (src == nullptr || sink == nullptr) return MTPV_ENULL;
+    if (!aligned(src, 16) || !aligned(sink, 4) || bytes % 16 != 0) return MTPV_EALIGN;
+    if (bytes == 0) return MTPV_OK;
+    if (launch_read(src, bytes, sink, static_cast<hipStream_t>(stream)) != hipSuccess) return MTPV_ELAUNCH;
+    return MTPV_OK;
+}
+
+int mtpv_mfma_rate(int iters, void* sink, int64_t* flops, void* stream) {
+    if (sink == nullptr || flops == nullptr) return MTPV_ENULL;
+    if (!aligned(sink, 4)) return MTPV_EALIGN;
+    if (iters < 1 || iters > (1 << 24)) return MTPV_EINVAL;
+    const int64_t f = launch_mfma_rate(iters, sink, static_cast<hipStream_t>(stream));
+    if (f < 0) return MTPV_ELAUNCH;
+    *flops = f;
+    return MTPV_OK;
+}
+
 }  // extern "C"

@@ -155,6 +155,11 @@ hipError_t launch_probs(const ProbsArgs& args, hipStream_t stream);
 
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 
+// Achievable-rate probes (ceiling.hip): one non-temporal read sweep of `bytes`; and
+// back-to-back bf16 MFMAs, returning the flops of the launch (-1 on a launch error).
+hipError_t launch_read(const void* src, size_t bytes, void* sink, hipStream_t stream);
+int64_t launch_mfma_rate(int iters, void* sink, hipStream_t stream);
+
 struct FuseArgs {
     const int32_t* tokens;  // [B]
     const uint8_t* embed;   // [V, H] bf16

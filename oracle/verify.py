@@ -84,7 +84,7 @@ def _assemble(drafts, a, fill):
 
 
 def greedy_verify(Lt, drafts):
-    """Greedy verification: keep the longest prefix that agrees with the target argmax.
+    """Greedy verification against the target argmax of every slot.
 
     The drafts are kept up to the first one the target disagrees with, so greedy
     speculative decoding emits the plain greedy sequence ("The Tiny Draft Model

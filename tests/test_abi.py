@@ -113,6 +113,26 @@ def test_calls_reject_bad_arguments_before_touching_the_device():
     assert L.mtpv_copy_bytes(ctypes.c_void_p(A), ctypes.c_void_p(A + 4), 16, None) == -2
 
 
+def test_rate_probes_validate_on_the_host():
+    """The achievable-rate probes reject NULL (MTPV_ENULL = -7), misaligned (-2) and
+    out-of-range (-1) arguments without launching; a zero-byte read launches nothing."""
+    L = mv.lib()
+    vp = ctypes.c_void_p
+    flops = ctypes.c_int64(-1)
+    assert L.mtpv_read_bytes(None, 16, vp(A), None) == -7
+    assert L.mtpv_read_bytes(vp(A), 16, None, None) == -7
+    assert L.mtpv_read_bytes(vp(A + 4), 16, vp(A), None) == -2
+    assert L.mtpv_read_bytes(vp(A), 24, vp(A), None) == -2
+    assert L.mtpv_read_bytes(vp(A), 16, vp(A + 2), None) == -2
+    assert L.mtpv_read_bytes(vp(A), 0, vp(A), None) == 0
+    assert L.mtpv_mfma_rate(16, None, ctypes.byref(flops), None) == -7
+    assert L.mtpv_mfma_rate(16, vp(A), None, None) == -7
+    assert L.mtpv_mfma_rate(16, vp(A + 1), ctypes.byref(flops), None) == -2
+    assert L.mtpv_mfma_rate(0, vp(A), ctypes.byref(flops), None) == -1
+    assert L.mtpv_mfma_rate((1 << 24) + 1, vp(A), ctypes.byref(flops), None) == -1
+    assert flops.value == -1
+
+
 def test_ragged_and_dual_calls_validate_on_the_host():
     """The per-request-length and dual entry points return the host-side errors (bad
     sizes, NULL or misaligned draft_len / greedy outputs, small workspace) without
