@@ -251,7 +251,7 @@ def achievable(W):
     t_mfma = median_s(lambda: mv.mfma_rate(iters, sink))
     return {"hbm_read_gbs": round(nbytes / t_read / 1e9, 1), "read_bytes": int(nbytes),
             "mfma_bf16_tflops": round(flops / t_mfma / 1e12, 1), "mfma_flops": int(flops),
-            "how": "mtpv_read_bytes over the head W (non-temporal 16-byte loads, contiguous ranges); "
+            "how": "mtpv_read_bytes over the head W (non-temporal 16-byte loads, 8 KB blocks per workgroup spaced by the grid); "
                    "mtpv_mfma_rate (4 waves per CU, 16 independent 16x16x32 bf16 MFMAs per round, varied "
                    "operand bits); median of 5 launches"}
 

@@ -346,7 +346,7 @@ MTPV_API int mtpv_copy_bytes(void* dst, const void* src, size_t bytes, void* str
  *
  * mtpv_read_bytes: one read sweep of `bytes` bytes at `src` (device pointer,
  * 16-byte aligned, bytes % 16 == 0; 0 bytes launches nothing) with 16-byte
- * non-temporal loads, each workgroup on its own contiguous range. `sink` is a
+ * non-temporal loads, each workgroup reading 8 KB blocks spaced by the grid. `sink` is a
  * 4-byte-aligned device word the kernel could write but never does. Errors:
  * MTPV_ENULL, MTPV_EALIGN, MTPV_ELAUNCH.
  *
