@@ -225,7 +225,8 @@ def roofline_of(alg_bytes, alg_flops, kern_s, traffic_bytes=None):
 
 def achievable(W):
     """What plain kernels reach on this machine beside the published peaks (measured after
-    the timed loop, outside it): one non-temporal read sweep of the head W's bytes,
+    the timed loop, outside it): one non-temporal read sweep of W's bytes (the head, or
+    the teacher logits of the draft loss),
     and back-to-back bf16 MFMAs (16x16x32) on every SIMD; median of 5 launches each,
     timed with events on the stream the library launches on."""
     import torch
@@ -392,6 +393,9 @@ def bench_loss(args):
                          "kernel_us": round(kern * 1e6, 2),
                          "algorithmic_bytes_per_launch": sel_bytes,
                          "call_frac": round(call_bytes / wall / 1e9 / HBM_PEAK_GBS, 4)}}
+    ach = achievable(Td)
+    line["roofline"]["achievable"] = ach
+    line["roofline"]["frac_of_achievable"] = round(line["roofline"]["achieved"] / ach["hbm_read_gbs"], 4)
     if not args.no_cpu_baseline:
         # the GPU's outputs of the timed call, compared row by row with the oracle's
         loss_h, idx_h = loss.cpu().numpy(), idx.cpu().numpy()
