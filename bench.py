@@ -285,7 +285,9 @@ def _events_time(fn, steps, warmup):
 
 def sweep(args):
     """Greedy verify against the number of head rows, H = 5120, V = 151936 (the
-    batched / depth-5 head): flat while HBM-bound, rising past the ridge."""
+    batched / depth-5 head): flat while HBM-bound, rising past the ridge. From 16 rows
+    on each line also times the bare head product through the library GEMM
+    (torch.mm, hipBLASLt: bf16 logits, no epilogue) on the same inputs."""
     import torch
     import mtp_draft_verification_amd as mv
     dev = torch.device("cuda:0")
@@ -305,10 +307,28 @@ def sweep(args):
         ws = mv.alloc_workspace(mv.MODE_GREEDY, B, k, H, V, mv.DTYPE_BF16, dev)
         wall, kern = _events_time(lambda: mv.spec_verify_greedy(xt_d, W, drafts, alen, out, ws), args.steps, args.warmup)
         alg_bytes = V * H * 2 + M * H * 2
-        print(json.dumps({"sweep": "greedy_verify_H5120_V151936", "M_eff": M, "B": B, "k": k,
-                          "ms_per_call": round(wall * 1e3, 4), "kernel_us": round(kern * 1e6, 2),
-                          "hbm_frac": round(alg_bytes / kern / 8e12, 4),
-                          "mfma_frac": round(2.0 * M * H * V / kern / 2.5e15, 4)}), flush=True)
+        line = {"sweep": "greedy_verify_H5120_V151936", "M_eff": M, "B": B, "k": k,
+                "ms_per_call": round(wall * 1e3, 4), "kernel_us": round(kern * 1e6, 2),
+                "hbm_frac": round(alg_bytes / kern / 8e12, 4),
+                "mfma_frac": round(2.0 * M * H * V / kern / 2.5e15, 4)}
+        if M >= 16:
+            # the same head product through the library GEMM (torch.mm -> hipBLASLt), bf16
+            # in and out, no epilogue: logits only, no softmax statistics or decisions
+            X = xt_d.reshape(M, H)
+            L = torch.empty((M, V), dtype=torch.bfloat16, device=dev)
+            for _ in range(args.warmup):
+                torch.mm(X, W.t(), out=L)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                torch.mm(X, W.t(), out=L)
+            e1.record()
+            torch.cuda.synchronize()
+            g = e0.elapsed_time(e1) / 1e3 / args.steps
+            line["library_gemm_us"] = round(g * 1e6, 2)
+            line["library_gemm_over_kernel"] = round(g / kern, 4)
+            del L
+        print(json.dumps(line), flush=True)
 
 
 def bench_fuse(args, wl):

@@ -7,7 +7,8 @@ decisions must stay below 0.1 % of the verified positions B (k + 1) of the run. 
 the first three steps a second call with the debug exports checks, on every row the
 head computes: logits within 2e-3 of the oracle's fp64 logits, probabilities within
 1e-5, argmax, and the decision path's own p(d) and q(d) (the values the acceptance
-test compares) within 1e-5.
+test compares) within 1e-5; on the first step a repeat of the call must reproduce every
+exported logit and argmax bit for bit.
 
 Drafts are drawn by the oracle from its fp64 drafter distribution (Philox word 2),
 so at the depth-5 chain workload the per-depth acceptance P(a >= d) of the GPU's
@@ -196,6 +197,15 @@ def _run(cid, mode):
         if s < DEBUG_STEPS:
             a2, out2 = _gpu_call(wl, mode, Wd, st["hidden"], drafts, s, ws, debug_ex=ex)
             assert np.array_equal(a2, a) and np.array_equal(out2, out)  # exports change nothing
+            if s == 0:
+                # the same call again: every exported logit and argmax bit for bit (fixed
+                # accumulation order, no atomics), the outcome unchanged
+                first_logits, first_argmax = ex["logits"].clone(), ex["argmax"].clone()
+                a3, out3 = _gpu_call(wl, mode, Wd, st["hidden"], drafts, s, ws, debug_ex=ex)
+                assert np.array_equal(a3, a) and np.array_equal(out3, out)
+                assert torch.equal(ex["logits"].view(torch.int32), first_logits.view(torch.int32))
+                assert torch.equal(ex["argmax"], first_argmax)
+                del first_logits, first_argmax
             dl, dp, dpd, dqd, ties = _check_debug_step(wl, mode, ex, ora, drafts)
             print(f"  step {s}: max|dlogit| {dl:.2e} max|dprob| {dp:.2e} max|dp(d)| {dpd:.2e} "
                   f"max|dq(d)| {dqd:.2e} argmax ties {ties}", flush=True)
