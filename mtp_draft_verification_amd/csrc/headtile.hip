@@ -259,13 +259,16 @@ __device__ __forceinline__ WStat frag_stats(const LmHeadArgs& p, const Item& t, 
             bi = obi;
         }
     }
+    // every argument is at most 0: the hardware exp2 (which flushes results below
+    // 2^-126, far below what a sum of at least 1 can hold) gives what the library exp2
+    // would, without its denormal-range guard
     float s = 0.f;
     if (mx != ninf) {
 #pragma unroll
         for (int fv = 0; fv < FV; ++fv)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                if (16 * fv + 4 * lgrp + q < t.vr) s += exp2f(a[fv][q] * c2 - mx);
+                if (16 * fv + 4 * lgrp + q < t.vr) s += __builtin_amdgcn_exp2f(a[fv][q] * c2 - mx);
     }
     s += __shfl_xor(s, 16);
     s += __shfl_xor(s, 32);
